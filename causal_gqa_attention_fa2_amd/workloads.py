@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module holds no attention arithmetic: it only draws lengths, tensors,
+block tables and paged pools. Both the HIP path and the CPU oracle are fed
+from it (through the tests, the benchmark and the smoke check), so the two
+sides always see bit-identical fp16 inputs.
+
+Recipe. Values are N(0, 1) drawn in fp32 from a CPU ``torch.Generator`` and
+rounded to fp16 (round-to-nearest-even). Draw order: lengths (or context
+lengths and the block permutation) first, then q, k, v, dO. Packed layouts:
+q, dO [T, H_q, d]; k, v [T, H_kv, d]; paged pools [num_blocks, 16, H_kv, d].
+
+Workloads (shapes of the RL.cu stack's Qwen3-0.6B attention; pitchhut
+"Project Highlights", mlllm.io "What happened"):
+
+* ``tiny``          B=1, S=64, H_q=2, H_kv=1, d=64
+* ``qwen3_train``   B=8, S=1024, H_q=16, H_kv=8, d=128
+* ``grpo_varlen``   4 prompts x 8 samples, prompt U{64..256} shared by a
+  prompt's samples, completion U{128..1024} per sample, packed prompt-major
+* ``long_context``  B=4, S=8192, H_q=16, H_kv=8, d=128
+* ``paged_decode``  256 sequences, ctx U{128..4096}, block 16, H_q=16,
+  H_kv=8, d=128; the logical blocks of all sequences (in order) receive a
+  seeded random permutation of the physical blocks.
+"""
+import math
+
+import torch
+
+TRAIN_WORKLOADS = {
+    "tiny": dict(seqlens=[64], h_q=2, h_kv=1, d=64, seed=1000),
+    "qwen3_train": dict(seqlens=[1024] * 8, h_q=16, h_kv=8, d=128, seed=1001),
+    "grpo_varlen": dict(seqlens=None, h_q=16, h_kv=8, d=128, seed=1002),
+    "long_context": dict(seqlens=[8192] * 4, h_q=16, h_kv=8, d=128, seed=1003),
+}
+DECODE_WORKLOADS = {
+    "paged_decode": dict(n=256, ctx_lo=128, ctx_hi=4096, block_size=16,
+                         h_q=16, h_kv=8, d=128, seed=1004),
+}
+BLOCK_SIZE = 16
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn_f16(shape, g, chunk=1 << 24):
+    """N(0,1) in fp32 rounded to fp16, drawn in chunks to bound host memory."""
+    out = torch.empty(shape, dtype=torch.float16)
+    flat = out.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n] = torch.randn(n, generator=g, dtype=torch.float32).half()
+    return out
+
+
+def grpo_seqlens(g, prompts=4, samples=8, prompt_range=(64, 256),
+                 completion_range=(128, 1024)):
+    """Sequence lengths of a GRPO group batch: one prompt length per prompt
+    shared by its samples, one completion length per sample."""
+    lens = []
+    for _ in range(prompts):
+        p = int(torch.randint(prompt_range[0], prompt_range[1] + 1, (1,), generator=g))
+        for _ in range(samples):
+            c = int(torch.randint(completion_range[0], completion_range[1] + 1, (1,),
+                                  generator=g))
+            lens.append(p + c)
+    return lens
+
+
+def cu_from_lens(seqlens):
+    cu = [0]
+    for L in seqlens:
+        cu.append(cu[-1] + int(L))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def make_train_inputs(seqlens, h_q, h_kv, d, seed, with_dout=True):
+    """Packed varlen q, k, v (and dO) in fp16 with their ``cu_seqlens``."""
+    g = _gen(seed)
+    if seqlens is None:
+        seqlens = grpo_seqlens(g)
+    cu = cu_from_lens(seqlens)
+    T = int(cu[-1])
+    q = _randn_f16((T, h_q, d), g)
+    k = _randn_f16((T, h_kv, d), g)
+    v = _randn_f16((T, h_kv, d), g)
+    dout = _randn_f16((T, h_q, d), g) if with_dout else None
+    return dict(q=q, k=k, v=v, dout=dout, cu_seqlens=cu, seqlens=list(seqlens),
+                max_seqlen=max(seqlens) if seqlens else 0, total_tokens=T,
+                h_q=h_q, h_kv=h_kv, d=d, scale=1.0 / math.sqrt(d))
+
+
+def workload_inputs(name, with_dout=True):
+    w = TRAIN_WORKLOADS[name]
+    return make_train_inputs(w["seqlens"], w["h_q"], w["h_kv"], w["d"], w["seed"],
+                             with_dout=with_dout)
+
+
+def make_decode_inputs(ctx_lens, h_q, h_kv, d, seed, block_size=BLOCK_SIZE,
+                       max_blocks=None, spare_blocks=0):
+    """Single-token queries and a paged pool holding each sequence's context.
+
+    Physical blocks: num_blocks = sum(ceil(ctx/bs)) + ``spare_blocks``. The
+    logical blocks of all sequences, taken in order, map through a seeded
+    random permutation; table entries past a sequence's last block hold -1.
+    """
+    g = _gen(seed)
+    ctx = [int(c) for c in ctx_lens]
+    nblk = [math.ceil(c / block_size) for c in ctx]
+    used = sum(nblk)
+    num_blocks = used + int(spare_blocks)
+    if max_blocks is None:
+        max_blocks = max(1, max(nblk) if nblk else 1)
+    perm = torch.randperm(num_blocks, generator=g)[:used].to(torch.int32)
+    table = torch.full((len(ctx), max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b, nb in enumerate(nblk):
+        table[b, :nb] = perm[pos:pos + nb]
+        pos += nb
+    n = len(ctx)
+    q = _randn_f16((n, h_q, d), g)
+    k_pool = _randn_f16((num_blocks, block_size, h_kv, d), g)
+    v_pool = _randn_f16((num_blocks, block_size, h_kv, d), g)
+    return dict(q=q, k_pool=k_pool, v_pool=v_pool, block_table=table,
+                ctx_lens=torch.tensor(ctx, dtype=torch.int32), n=n, h_q=h_q,
+                h_kv=h_kv, d=d, block_size=block_size, num_blocks=num_blocks,
+                max_blocks=max_blocks, max_ctx=max(ctx) if ctx else 0,
+                scale=1.0 / math.sqrt(d))
+
+
+def decode_workload_inputs(name="paged_decode"):
+    w = DECODE_WORKLOADS[name]
+    g = _gen(w["seed"])
+    ctx = torch.randint(w["ctx_lo"], w["ctx_hi"] + 1, (w["n"],), generator=g).tolist()
+    max_blocks = math.ceil(w["ctx_hi"] / w["block_size"])
+    return make_decode_inputs(ctx, w["h_q"], w["h_kv"], w["d"], w["seed"] + 7919,
+                              block_size=w["block_size"], max_blocks=max_blocks)
+
+
+def poison_unused(inp):
+    """NaN into every pool slot no sequence uses (tail slots of last blocks,
+    spare blocks). Returns a new dict with cloned pools."""
+    k_pool = inp["k_pool"].clone()
+    v_pool = inp["v_pool"].clone()
+    bs = inp["block_size"]
+    used = torch.zeros(k_pool.shape[0], bs, dtype=torch.bool)
+    for b in range(inp["n"]):
+        c = int(inp["ctx_lens"][b])
+        for lb in range(math.ceil(c / bs)):
+            phys = int(inp["block_table"][b, lb])
+            used[phys, :min(bs, c - lb * bs)] = True
+    k_pool[~used] = float("nan")
+    v_pool[~used] = float("nan")
+    out = dict(inp)
+    out.update(k_pool=k_pool, v_pool=v_pool)
+    return out
