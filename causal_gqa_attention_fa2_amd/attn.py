@@ -1,0 +1,242 @@
+"""Thin Python binding of libattn.so (include/attn.h).
+
+Argument marshalling only: checks dtypes, shapes, devices and contiguity of
+torch tensors, passes raw device pointers and the current HIP stream to the
+C ABI, and raises ``AttnError`` on a non-OK status. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If the
+library has not been built, every call raises.
+
+Names follow the C ABI: ``fwd`` -> attn_fwd, ``bwd`` -> attn_bwd,
+``decode_paged`` -> attn_decode_paged.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+                3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
+            "attn_decode_workspace_bytes", "attn_status_string", "attn_check_cu_seqlens",
+            "attn_check_paged")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)}")
+
+
+class VarlenDims(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class PagedDims(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_ctx_len", ctypes.c_int32)]
+
+
+_LIB = None
+_vp = ctypes.c_void_p
+
+
+def load_library():
+    """Load libattn.so once (after torch, so both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python -m causal_gqa_attention_fa2_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.attn_fwd.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, ctypes.c_float,
+                             _vp, _vp, _vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(VarlenDims)]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(PagedDims)]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_paged.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+    lib.attn_decode_paged.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_check_cu_seqlens.argtypes = [ctypes.POINTER(VarlenDims), _vp]
+    lib.attn_check_cu_seqlens.restype = ctypes.c_int
+    lib.attn_check_paged.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp]
+    lib.attn_check_paged.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _check(fn, status):
+    if status != ATTN_OK:
+        raise AttnError(fn, status)
+
+
+def varlen_dims(q, k, cu_seqlens, max_seqlen=None):
+    T, h_q, d = q.shape
+    if max_seqlen is None:  # host copy: synchronises, meant for tests
+        cu = cu_seqlens.cpu()
+        max_seqlen = int((cu[1:] - cu[:-1]).max()) if cu.numel() > 1 else 0
+    return VarlenDims(cu_seqlens.numel() - 1, T, int(max_seqlen), h_q, k.shape[1], d)
+
+
+def fwd(q, k, v, cu_seqlens, scale=None, o=None, lse=None, max_seqlen=None):
+    """attn_fwd: returns (o fp16 [T, h_q, d], lse fp32 [h_q, T])."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.float16, 3)
+    _need(k, "k", torch.float16, 3, dev)
+    _need(v, "v", torch.float16, 3, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    T, h_q, d = q.shape
+    if k.shape != v.shape or k.shape[0] != T or k.shape[2] != d:
+        raise ValueError("k, v must be [T, h_kv, d] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((h_q, T), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    if o.shape != q.shape or lse.shape != (h_q, T):
+        raise ValueError("o / lse shape mismatch")
+    dims = varlen_dims(q, k, cu_seqlens, max_seqlen)
+    _check("attn_fwd", lib.attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(cu_seqlens), float(scale), _ptr(o), _ptr(lse),
+                                    _stream()))
+    return o, lse
+
+
+def bwd_workspace_bytes(dims):
+    return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def bwd(q, k, v, o, lse, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None,
+        max_seqlen=None, workspace=None):
+    """attn_bwd: returns (dq, dk, dv) in fp16."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.float16, 3)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, torch.float16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    T, h_q, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or \
+            lse.shape != (h_q, T) or k.shape[0] != T or k.shape[2] != d:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.float16, 3, dev)
+    _need(dk, "dk", torch.float16, 3, dev)
+    _need(dv, "dv", torch.float16, 3, dev)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shape mismatch")
+    dims = varlen_dims(q, k, cu_seqlens, max_seqlen)
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    _check("attn_bwd", lib.attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    _ptr(lse), _ptr(dout), _ptr(cu_seqlens), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), float(scale), _ptr(workspace),
+                                    workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def paged_dims(q, k_pool, block_table, max_ctx_len):
+    n, h_q, d = q.shape
+    nb, bs, h_kv, _ = k_pool.shape
+    return PagedDims(n, h_q, h_kv, d, bs, block_table.shape[1], nb, int(max_ctx_len))
+
+
+def decode_workspace_bytes(dims):
+    return int(load_library().attn_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, scale=None, o=None,
+                 max_ctx_len=None, workspace=None):
+    """attn_decode_paged: returns o fp16 [n, h_q, d]."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.float16, 3)
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    n, h_q, d = q.shape
+    if k_pool.shape != v_pool.shape or k_pool.shape[3] != d or block_table.shape[0] != n or \
+            ctx_lens.shape[0] != n:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if max_ctx_len is None:  # host copy: synchronises, meant for tests
+        max_ctx_len = int(ctx_lens.max()) if n else 0
+    o = torch.empty_like(q) if o is None else o
+    _need(o, "o", torch.float16, 3, dev)
+    if o.shape != q.shape:
+        raise ValueError("o shape mismatch")
+    dims = paged_dims(q, k_pool, block_table, max_ctx_len)
+    need = int(lib.attn_decode_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    _check("attn_decode_paged",
+           lib.attn_decode_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(block_table), _ptr(ctx_lens), _ptr(o), float(scale),
+                                 _ptr(workspace), workspace.numel(), _stream()))
+    return o
+
+
+def check_cu_seqlens_host(dims, cu_host):
+    """attn_check_cu_seqlens on a host int32 tensor."""
+    cu_host = cu_host.to(torch.int32).contiguous()
+    return int(load_library().attn_check_cu_seqlens(ctypes.byref(dims), _vp(cu_host.data_ptr())))
+
+
+def check_paged_host(dims, block_table_host, ctx_host):
+    """attn_check_paged on host int32 tensors."""
+    bt = block_table_host.to(torch.int32).contiguous()
+    cx = ctx_host.to(torch.int32).contiguous()
+    return int(load_library().attn_check_paged(ctypes.byref(dims), _vp(bt.data_ptr()),
+                                               _vp(cx.data_ptr())))

@@ -1,0 +1,233 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument checks,
+// workspace sizing and the hand-off to the kernel launchers. Host code only;
+// the kernels live in the .hip files.
+#include "attn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by forward and backward. Sets *empty for a batch with
+// nothing to compute.
+attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
+  if (!d) return ATTN_ERR_INVALID_ARG;
+  if (d->n_seqs < 0 || d->total_tokens < 0 || d->max_seqlen < 0) return ATTN_ERR_INVALID_ARG;
+  if (d->h_q <= 0 || d->h_kv <= 0 || d->head_dim <= 0) return ATTN_ERR_INVALID_ARG;
+  if (d->h_q % d->h_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d->h_q / d->h_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (d->max_seqlen > d->total_tokens) return ATTN_ERR_INVALID_ARG;
+  if (d->n_seqs > 0 && d->total_tokens > 0 && d->max_seqlen == 0) return ATTN_ERR_INVALID_ARG;
+  // Element offsets are formed in 64-bit, token indices in 32-bit.
+  if ((int64_t)d->total_tokens * d->h_q > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  *empty = d->n_seqs == 0 || d->total_tokens == 0;
+  return ATTN_OK;
+}
+
+size_t bwd_ws_parts(const attn_varlen_dims* d, size_t* acc_bytes) {
+  const size_t acc = (size_t)d->total_tokens * d->h_q * d->head_dim * sizeof(float);
+  const size_t row = (size_t)d->h_q * d->total_tokens * sizeof(float);
+  *acc_bytes = align_up(acc);
+  return align_up(acc) + align_up(row);
+}
+
+attn_status check_paged(const attn_paged_dims* d, bool* empty) {
+  if (!d) return ATTN_ERR_INVALID_ARG;
+  if (d->n_seqs < 0 || d->h_q <= 0 || d->h_kv <= 0 || d->head_dim <= 0) return ATTN_ERR_INVALID_ARG;
+  if (d->max_blocks_per_seq < 0 || d->num_blocks < 0 || d->max_ctx_len < 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (d->h_q % d->h_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d->h_q / d->h_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (d->block_size != 16) return ATTN_ERR_UNSUPPORTED;
+  if (d->n_seqs > 65535 || d->h_kv > 65535) return ATTN_ERR_UNSUPPORTED;  // grid y/z limits
+  if ((int64_t)d->max_blocks_per_seq * 16 < d->max_ctx_len) return ATTN_ERR_INVALID_ARG;
+  *empty = d->n_seqs == 0;
+  // A non-empty context needs at least one pool block.
+  if (!*empty && d->max_ctx_len > 0 && d->num_blocks == 0) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int decode_max_splits(const attn_paged_dims* d) {
+  return (d->max_ctx_len + cgqa::kDecodeSplit - 1) / cgqa::kDecodeSplit;
+}
+
+size_t decode_ws_parts(const attn_paged_dims* d, size_t* o_bytes) {
+  const size_t slots = (size_t)d->n_seqs * d->h_q * decode_max_splits(d);
+  *o_bytes = align_up(slots * d->head_dim * sizeof(float));
+  return *o_bytes + align_up(slots * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_UNKNOWN_STATUS";
+}
+
+attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens, float scale, void* o, float* lse, void* stream) {
+  bool empty = false;
+  attn_status st = check_varlen(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!q || !k || !v || !cu_seqlens || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      ((uintptr_t)cu_seqlens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.lse = lse;
+  a.n_seqs = dims->n_seqs;
+  a.total_tokens = dims->total_tokens;
+  a.max_seqlen = dims->max_seqlen;
+  a.h_q = dims->h_q;
+  a.h_kv = dims->h_kv;
+  a.head_dim = dims->head_dim;
+  a.scale = scale;
+  return cgqa::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims) {
+  bool empty = false;
+  if (check_varlen(dims, &empty) != ATTN_OK || empty) return 0;
+  size_t acc;
+  return bwd_ws_parts(dims, &acc);
+}
+
+attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dO,
+                     const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  attn_status st = check_varlen(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !cu_seqlens || !dq || !dk || !dv)
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      ((uintptr_t)cu_seqlens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  size_t acc_bytes;
+  const size_t need = bwd_ws_parts(dims, &acc_bytes);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign))
+    return ATTN_ERR_WORKSPACE;
+  cgqa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dO;
+  a.cu_seqlens = cu_seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = (float*)workspace;
+  a.drow = (float*)((char*)workspace + acc_bytes);
+  a.n_seqs = dims->n_seqs;
+  a.total_tokens = dims->total_tokens;
+  a.max_seqlen = dims->max_seqlen;
+  a.h_q = dims->h_q;
+  a.h_kv = dims->h_kv;
+  a.head_dim = dims->head_dim;
+  a.scale = scale;
+  return cgqa::launch_bwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_decode_workspace_bytes(const attn_paged_dims* dims) {
+  bool empty = false;
+  if (check_paged(dims, &empty) != ATTN_OK || empty) return 0;
+  size_t ob;
+  return decode_ws_parts(dims, &ob);
+}
+
+attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* ctx_lens, void* o, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  attn_status st = check_paged(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!q || !ctx_lens || !o) return ATTN_ERR_INVALID_ARG;
+  if (dims->max_ctx_len > 0 && (!k_pool || !v_pool || !block_table)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  size_t ob;
+  const size_t need = decode_ws_parts(dims, &ob);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign)))
+    return ATTN_ERR_WORKSPACE;
+  cgqa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.o = o;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + ob);
+  a.n_seqs = dims->n_seqs;
+  a.h_q = dims->h_q;
+  a.h_kv = dims->h_kv;
+  a.head_dim = dims->head_dim;
+  a.max_blocks_per_seq = dims->max_blocks_per_seq;
+  a.max_splits = decode_max_splits(dims);
+  a.scale = scale;
+  return cgqa::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu) {
+  if (!dims || !cu || dims->n_seqs < 0) return ATTN_ERR_INVALID_ARG;
+  if (cu[0] != 0) return ATTN_ERR_INVALID_ARG;
+  int32_t mx = 0;
+  for (int32_t b = 0; b < dims->n_seqs; ++b) {
+    const int32_t len = cu[b + 1] - cu[b];
+    if (cu[b + 1] < cu[b]) return ATTN_ERR_INVALID_ARG;
+    if (len > mx) mx = len;
+  }
+  if (cu[dims->n_seqs] != dims->total_tokens) return ATTN_ERR_INVALID_ARG;
+  if (mx > dims->max_seqlen) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+attn_status attn_check_paged(const attn_paged_dims* dims, const int32_t* table,
+                             const int32_t* ctx) {
+  if (!dims || !ctx || dims->n_seqs < 0 || dims->block_size <= 0) return ATTN_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < dims->n_seqs; ++b) {
+    const int32_t c = ctx[b];
+    if (c < 0 || c > dims->max_ctx_len) return ATTN_ERR_INVALID_ARG;
+    const int32_t nb = (c + dims->block_size - 1) / dims->block_size;
+    if (nb > dims->max_blocks_per_seq) return ATTN_ERR_INVALID_ARG;
+    if (nb > 0 && !table) return ATTN_ERR_INVALID_ARG;
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t e = table[(size_t)b * dims->max_blocks_per_seq + j];
+      if (e < 0 || e >= dims->num_blocks) return ATTN_ERR_INVALID_ARG;
+    }
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// cdna4.h -- small device helpers for gfx950 (CDNA4): fp16 MFMA, LDS transpose
+// reads and half-wave exchanges. Lane layouts below were checked on the
+// hardware with an in-bounds probe.
+//
+// v_mfma_f32_32x32x16_f16 (one wave, 64 lanes; l32 = lane % 32, hi = lane / 32):
+//   A operand (8 halves): A[row = l32][k = 8*hi + s], s = 0..7
+//   B operand (8 halves): B[k = 8*hi + s][col = l32]
+//   C/D (16 floats):      C[row = 8*(i/4) + 4*hi + (i%4)][col = l32], i = 0..15
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j returns element e
+//   (e = 0..3) of the 4-element chunk addressed by lane 4*e + j/4, taken at
+//   position j%4. If lane j of a group addresses row (r0 + j/4), column
+//   (c0 + 4*(j%4)) of a row-major fp16 tile, lane j receives column c0 + j of
+//   rows r0..r0+3 -- a 4x16 transpose straight out of LDS.
+// v_permlane32_swap(x, x) returns {x[lane], x[lane ^ 32]} in some order, so
+//   max/sum of the two halves of a wave takes one exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgqa {
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_raw __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima start at this finite value (not -inf) so that a row whose
+// scores are all masked never computes (-inf) - (-inf).
+constexpr float kMaxInit = -1.0e30f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16 on an LDS address.
+__device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
+  fp16x4_raw r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (__attribute__((address_space(3))) fp16x4_raw*)(p));
+  return __builtin_bit_cast(f16x4, r);
+}
+
+__device__ __forceinline__ f16x8 cat4(f16x4 a, f16x4 b) {
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f16x8 zero_f16x8() { return f16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+}  // namespace cgqa

@@ -1,0 +1,177 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention library.
+ *
+ * What the library computes. The RL.cu project pages (pitchhut "Project
+ * Highlights"; mlllm.io "What happened") name hand-written FlashAttention-2
+ * forward and backward kernels and an inference engine with a paged key/value
+ * cache (pitchhut "Key Features", items 1-2), with FP16 inputs and FP32
+ * accumulation (pitchhut "Key Features", item 1). FlashAttention-2 is exact
+ * softmax attention, so every entry point below returns, up to floating-point
+ * rounding, the plain definition:
+ *
+ *   S_ij = scale * <q_i, k_j>  for key position j <= query position i
+ *          (positions counted from the start of each packed sequence),
+ *   LSE_i = ln sum_j exp(S_ij),   O_i = sum_j exp(S_ij - LSE_i) v_j,
+ *
+ * with query head h reading key/value head h / (h_q / h_kv) (contiguous
+ * grouped-query groups). Attention never crosses a sequence boundary.
+ *
+ * Conventions shared by every entry point.
+ *  - Tensor arguments are DEVICE pointers to dense row-major arrays; fp16 is
+ *    IEEE binary16, fp32 is IEEE binary32. Every tensor pointer must be
+ *    16-byte aligned.
+ *  - The caller owns every buffer (inputs, outputs, workspace). The library
+ *    never allocates, frees or keeps a pointer after the call returns, never
+ *    synchronizes and never copies device data to the host.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *    stream) and the call returns before it finishes. Calls are stateless and
+ *    may be captured into a HIP graph.
+ *  - Argument checks run before any HIP call. A failed check returns a
+ *    status code and enqueues nothing. A launch failure reported by the HIP
+ *    runtime returns ATTN_ERR_HIP. Faults inside kernels surface at the
+ *    caller's next synchronization. Nothing aborts or throws across the ABI.
+ *  - The contents of device index arrays (cu_seqlens, block_table, ctx_lens)
+ *    are NOT checked by the compute entry points; attn_check_cu_seqlens and
+ *    attn_check_paged check host copies of them.
+ */
+#ifndef CGQA_ATTN_H
+#define CGQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer  */
+    ATTN_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, group size above 16,
+                                 block size not 16                           */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
+    ATTN_ERR_HIP = 4          /* the HIP runtime reported a launch error     */
+} attn_status;
+
+/* Shape of a packed variable-length batch of n_seqs sequences.
+ *   total_tokens = cu_seqlens[n_seqs] (T), max_seqlen = max sequence length,
+ *   h_q query heads, h_kv key/value heads (h_q % h_kv == 0, h_q / h_kv <= 16),
+ *   head_dim in {64, 128}.
+ * total_tokens and max_seqlen are host copies so no device read is needed to
+ * size the launch; they must agree with cu_seqlens. n_seqs = 0 or
+ * total_tokens = 0 is a valid empty batch (nothing is enqueued). */
+typedef struct attn_varlen_dims {
+    int32_t n_seqs;
+    int32_t total_tokens;
+    int32_t max_seqlen;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t head_dim;
+} attn_varlen_dims;
+
+/* Shape of a paged decode batch: n_seqs sequences with one query token each,
+ * pools of num_blocks blocks of block_size (= 16) tokens, a block table of
+ * max_blocks_per_seq entries per sequence, and max_ctx_len >= every ctx_lens
+ * entry (host copy, sizes the launch and the workspace). */
+typedef struct attn_paged_dims {
+    int32_t n_seqs;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    int32_t num_blocks;
+    int32_t max_ctx_len;
+} attn_paged_dims;
+
+/*
+ * attn_fwd -- causal GQA attention forward over a packed varlen batch
+ * (FlashAttention-2 forward: online softmax, saved log-sum-exp; pitchhut
+ * "Project Highlights").
+ *   q          fp16 [T, h_q, d]          queries
+ *   k, v       fp16 [T, h_kv, d]         keys, values
+ *   cu_seqlens int32 [n_seqs + 1]        0 = cu[0] <= cu[1] <= ... = T
+ *   scale      multiplies q.k before the softmax (usually 1/sqrt(d))
+ *   o          fp16 [T, h_q, d]          output, fully overwritten
+ *   lse        fp32 [h_q, T]             natural-log log-sum-exp of the scaled
+ *                                        scores of each (head, token) row,
+ *                                        fully overwritten; attn_bwd needs it
+ * Rounding: fp32 accumulation, softmax weights rounded to fp16 before the
+ * weighted sum of values, O rounded to nearest-even fp16.
+ * Runs are bitwise reproducible for identical inputs.
+ */
+attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
+                     const void* v, const int32_t* cu_seqlens, float scale, void* o,
+                     float* lse, void* stream);
+
+/* Bytes of device workspace attn_bwd needs for `dims` (0 for an empty
+ * batch). Holds an fp32 dQ accumulator [T, h_q, d] and the fp32 row terms
+ * D = rowsum(dO * O) [h_q, T]. */
+size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims);
+
+/*
+ * attn_bwd -- backward of attn_fwd for the loss <O, dO> (FlashAttention-2
+ * backward, dQ/dK/dV by recomputing the softmax from the saved LSE; pitchhut
+ * "Project Highlights", gradient checkpointing in "Key Features" item 3).
+ *   q, k, v, cu_seqlens, scale   as given to attn_fwd (same scale)
+ *   o          fp16 [T, h_q, d]   attn_fwd's output
+ *   lse        fp32 [h_q, T]      attn_fwd's log-sum-exp
+ *   dO         fp16 [T, h_q, d]   cotangent of O (no cotangent on the LSE)
+ *   dq         fp16 [T, h_q, d]   outputs, fully overwritten (no zeroing
+ *   dk, dv     fp16 [T, h_kv, d]  needed); dk and dv sum over the group's
+ *                                 query heads
+ *   workspace  device buffer of at least attn_bwd_workspace_bytes(dims)
+ *              bytes, 256-byte aligned; the library initialises it.
+ * dq accumulates with fp32 atomics, so its low bits may differ run to run.
+ */
+attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* dO,
+                     const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace attn_decode_paged needs for `dims`: fp32
+ * per-split partial outputs, maxima and sums. */
+size_t attn_decode_workspace_bytes(const attn_paged_dims* dims);
+
+/*
+ * attn_decode_paged -- single-token decode attention over a paged key/value
+ * cache (the rollout engine's "paged key-value caching"; pitchhut "Key
+ * Features" item 2, mlllm.io "What happened").
+ *   q           fp16 [n, h_q, d]            one query token per sequence
+ *   k_pool      fp16 [num_blocks, 16, h_kv, d]   key pool
+ *   v_pool      fp16 [num_blocks, 16, h_kv, d]   value pool
+ *   block_table int32 [n, max_blocks_per_seq]  physical block of each logical
+ *               block; entries past ceil(ctx/16) are never read
+ *   ctx_lens    int32 [n]   context length of each sequence (0..max_ctx_len)
+ *   o           fp16 [n, h_q, d]   output, fully overwritten; a zero-length
+ *               context yields a zero row
+ *   scale       multiplies q.k (usually 1/sqrt(d))
+ *   workspace   at least attn_decode_workspace_bytes(dims) bytes
+ * Position t of sequence b is slot t % 16 of block block_table[b][t / 16].
+ * Pool slots past a sequence's context are never read.
+ */
+attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* ctx_lens, void* o, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status status);
+
+/* Host-side check of a HOST copy of cu_seqlens against dims: cu[0] == 0,
+ * non-decreasing, cu[n] == total_tokens, every length <= max_seqlen.
+ * Returns ATTN_OK or ATTN_ERR_INVALID_ARG. Makes no HIP call. */
+attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu_host);
+
+/* Host-side check of HOST copies of block_table and ctx_lens against dims:
+ * 0 <= ctx <= max_ctx_len, ceil(ctx/16) <= max_blocks_per_seq and every used
+ * entry in [0, num_blocks). Returns ATTN_OK or ATTN_ERR_INVALID_ARG. */
+attn_status attn_check_paged(const attn_paged_dims* dims, const int32_t* block_table_host,
+                             const int32_t* ctx_lens_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGQA_ATTN_H */

@@ -1,0 +1,147 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library loads, exports every function include/attn.h declares, and
+rejects bad arguments with the documented status codes before making any
+HIP call. Only failing or empty calls are made here, so no kernel launches.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import causal_gqa_attention_fa2_amd as A
+from causal_gqa_attention_fa2_amd.attn import PagedDims, VarlenDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # an aligned non-null address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_fwd", "attn_bwd", "attn_decode_paged"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in A.attn.STATUS_NAMES.items():
+        assert lib.attn_status_string(code).decode() == name
+    assert lib.attn_status_string(99).decode() == "ATTN_UNKNOWN_STATUS"
+
+
+def _fwd(lib, dims, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE):
+    p = ctypes.c_void_p
+    return lib.attn_fwd(ctypes.byref(dims) if dims is not None else None, p(q), p(k), p(v),
+                        p(cu), 0.1, p(o), p(lse), None)
+
+
+def test_fwd_argument_checks(lib):
+    good = dict(n_seqs=2, total_tokens=100, max_seqlen=60, h_q=16, h_kv=8, head_dim=128)
+    assert _fwd(lib, None) == INVALID
+    for field, bad, code in [("h_q", 15, INVALID), ("head_dim", 96, UNSUPPORTED),
+                             ("head_dim", 256, UNSUPPORTED), ("h_kv", 0, INVALID),
+                             ("n_seqs", -1, INVALID), ("max_seqlen", 101, INVALID),
+                             ("max_seqlen", 0, INVALID), ("total_tokens", -5, INVALID)]:
+        d = dict(good)
+        d[field] = bad
+        assert _fwd(lib, VarlenDims(**d)) == code, (field, bad)
+    d = dict(good, h_q=17 * 2, h_kv=2)  # group of 17 query heads
+    assert _fwd(lib, VarlenDims(**d)) == UNSUPPORTED
+    dims = VarlenDims(**good)
+    assert _fwd(lib, dims, q=0) == INVALID
+    assert _fwd(lib, dims, lse=0) == INVALID
+    assert _fwd(lib, dims, o=FAKE + 8) == INVALID     # misaligned
+    assert _fwd(lib, dims, cu=FAKE + 2) == INVALID    # misaligned int32
+    # Empty batches succeed without touching the (null) pointers.
+    assert _fwd(lib, VarlenDims(0, 0, 0, 16, 8, 128), 0, 0, 0, 0, 0, 0) == OK
+    assert _fwd(lib, VarlenDims(3, 0, 0, 16, 8, 128), 0, 0, 0, 0, 0, 0) == OK
+
+
+def test_bwd_workspace(lib):
+    dims = VarlenDims(2, 100, 60, 16, 8, 128)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(dims))
+    acc = 100 * 16 * 128 * 4
+    acc = (acc + 255) // 256 * 256
+    row = (16 * 100 * 4 + 255) // 256 * 256
+    assert need == acc + row
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(0, 0, 0, 16, 8, 128))) == 0
+    p = ctypes.c_void_p
+    args = [p(FAKE)] * 7 + [p(FAKE)] * 3
+
+    def call(ws, nbytes):
+        return lib.attn_bwd(ctypes.byref(dims), *args, 0.1, p(ws), nbytes, None)
+
+    assert call(0, need) == WORKSPACE
+    assert call(FAKE, need - 1) == WORKSPACE
+    assert call(FAKE + 16, need) == WORKSPACE  # workspace must be 256-byte aligned
+    bad = VarlenDims(2, 100, 60, 16, 8, 80)
+    assert lib.attn_bwd(ctypes.byref(bad), *args, 0.1, p(FAKE), need, None) == UNSUPPORTED
+
+
+def test_decode_argument_checks(lib):
+    dims = PagedDims(4, 16, 8, 128, 16, 256, 1000, 4096)
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(dims))
+    splits = 4096 // 512
+    slots = 4 * 16 * splits
+    assert need == (slots * 128 * 4 + 255) // 256 * 256 + (slots * 2 * 4 + 255) // 256 * 256
+    p = ctypes.c_void_p
+
+    def call(d, ws=FAKE, nbytes=None, q=FAKE, bt=FAKE):
+        return lib.attn_decode_paged(ctypes.byref(d), p(q), p(FAKE), p(FAKE), p(bt), p(FAKE),
+                                     p(FAKE), 0.1, p(ws), need if nbytes is None else nbytes,
+                                     None)
+
+    assert call(PagedDims(4, 16, 8, 128, 32, 256, 1000, 4096)) == UNSUPPORTED
+    assert call(PagedDims(4, 16, 8, 128, 16, 100, 1000, 4096)) == INVALID  # table too short
+    assert call(PagedDims(4, 16, 6, 128, 16, 256, 1000, 4096)) == INVALID
+    assert call(PagedDims(4, 16, 8, 128, 16, 256, 0, 4096)) == INVALID
+    assert call(dims, q=0) == INVALID
+    assert call(dims, bt=FAKE + 1) == INVALID
+    assert call(dims, ws=0) == WORKSPACE
+    assert call(dims, nbytes=need - 4) == WORKSPACE
+    assert call(PagedDims(0, 16, 8, 128, 16, 256, 1000, 4096), ws=0, nbytes=0) == OK
+
+
+def test_host_validators():
+    dims = VarlenDims(3, 10, 7, 4, 2, 64)
+    ok = torch.tensor([0, 3, 3, 10], dtype=torch.int32)
+    assert A.attn.check_cu_seqlens_host(dims, ok) == OK
+    assert A.attn.check_cu_seqlens_host(dims, torch.tensor([1, 3, 3, 10])) == INVALID
+    assert A.attn.check_cu_seqlens_host(dims, torch.tensor([0, 3, 2, 10])) == INVALID
+    assert A.attn.check_cu_seqlens_host(dims, torch.tensor([0, 3, 3, 9])) == INVALID
+    assert A.attn.check_cu_seqlens_host(VarlenDims(3, 10, 6, 4, 2, 64), ok) == INVALID
+    pd = PagedDims(2, 4, 2, 64, 16, 3, 5, 40)
+    bt = torch.tensor([[4, 0, -1], [1, 2, 3]], dtype=torch.int32)
+    assert A.attn.check_paged_host(pd, bt, torch.tensor([17, 40])) == OK
+    assert A.attn.check_paged_host(pd, bt, torch.tensor([33, 40])) == INVALID  # entry -1 used
+    assert A.attn.check_paged_host(pd, bt, torch.tensor([17, 41])) == INVALID  # > max ctx
+    bt2 = bt.clone()
+    bt2[1, 2] = 5
+    assert A.attn.check_paged_host(pd, bt2, torch.tensor([17, 40])) == INVALID  # out of pool
+    assert A.attn.check_paged_host(pd, bt, torch.tensor([0, 0])) == OK
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(4, 2, 64, dtype=torch.float16)
+    k = torch.zeros(4, 1, 64, dtype=torch.float16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        A.fwd(q, k, k, cu)
+    with pytest.raises(TypeError):
+        A.fwd(q.float(), k, k, cu)
