@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal GQA attention hot path on one MI355X.
+
+One step = one pass over every stage of the path on resident synthetic
+inputs: attn_fwd + attn_bwd on the Qwen3-0.6B training workload (B=8,
+S=1024, H_q=16, H_kv=8, d=128, fp16) and attn_decode_paged on the rollout
+decode workload (256 sequences, ctx U{128..4096}, 16-token blocks).
+
+Prints ONE JSON line. ``value`` is the forward+backward attention
+throughput in TFLOP/s (causal FLOP count: 4*d*H_q per unmasked (query, key)
+pair for the forward, 2.5x that for the backward) from HIP events on the
+launch stream; the decode bandwidth (algorithmic bytes / event time) rides
+along in ``decode``. ``roofline`` reports the kernel that takes the most time
+per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same training workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense fp16
+HBM_PEAK_GBPS = 8000.0
+TRAIN_WORKLOAD = "qwen3_train"
+DECODE_WORKLOAD = "paged_decode"
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "cdna4.h", "kernels.h",
+                  "attn_api.cpp"]
+
+
+def causal_pairs(seqlens):
+    return sum(L * (L + 1) // 2 for L in seqlens)
+
+
+def train_costs(inp):
+    d, h_q, h_kv, T = inp["d"], inp["h_q"], inp["h_kv"], inp["total_tokens"]
+    pairs = causal_pairs(inp["seqlens"])
+    f_fwd = 4 * d * h_q * pairs
+    f_bwd = 2.5 * f_fwd
+    qo = T * h_q * d * 2
+    kv = T * h_kv * d * 2
+    lse = h_q * T * 4
+    b_fwd = qo + 2 * kv + qo + lse                       # read q,k,v; write o,lse
+    b_bwd = qo + 2 * kv + qo + qo + lse + qo + 2 * kv     # read q,k,v,o,dO,lse; write dq,dk,dv
+    return f_fwd, f_bwd, b_fwd, b_bwd
+
+
+def decode_costs(inp):
+    ctx = [int(c) for c in inp["ctx_lens"]]
+    d, h_q, h_kv, n = inp["d"], inp["h_q"], inp["h_kv"], inp["n"]
+    kv = sum(ctx) * h_kv * d * 2 * 2
+    qo = 2 * n * h_q * d * 2
+    table = sum(math.ceil(c / inp["block_size"]) for c in ctx) * 4 + n * 4
+    flops = 4 * d * h_q * sum(ctx)
+    return flops, kv + qo + table
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_gqa_attention_fa2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(budget_s):
+    """The fp64 oracle (as it stands) on whole (sequence, KV-group) slices of the
+    training workload, forward + backward, until `budget_s` seconds pass."""
+    import numpy as np
+    from causal_gqa_attention_fa2_amd import workloads as W
+    from oracle import attn_bwd_ref, attn_fwd_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    inp = W.workload_inputs(TRAIN_WORKLOAD)
+    cu = inp["cu_seqlens"].tolist()
+    G = inp["h_q"] // inp["h_kv"]
+    flops = 0.0
+    n = 0
+    slices = [(b, g) for b in range(len(cu) - 1) for g in range(inp["h_kv"])]
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:  # whole passes over the slices, then stop
+        for b, g in slices:
+            s, e = cu[b], cu[b + 1]
+            hs = slice(g * G, (g + 1) * G)
+            q = inp["q"][s:e, hs].numpy()
+            k = inp["k"][s:e, g:g + 1].numpy()
+            v = inp["v"][s:e, g:g + 1].numpy()
+            do = inp["dout"][s:e, hs].numpy()
+            attn_fwd_ref(q, k, v, [0, e - s], inp["scale"])
+            attn_bwd_ref(q, k, v, do, [0, e - s], inp["scale"])
+            flops += 3.5 * 4 * inp["d"] * G * causal_pairs([e - s])
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} (sequence, KV-group) slices of {TRAIN_WORKLOAD} "
+                      f"({len(slices)} per batch), fwd+bwd in fp64, {dt:.1f} s wall",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the attention path here runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_gqa_attention_fa2_amd as attn
+    from causal_gqa_attention_fa2_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    tr = W.workload_inputs(TRAIN_WORKLOAD)
+    de = W.decode_workload_inputs(DECODE_WORKLOAD)
+    q, k, v, dout = (tr[n].to(dev) for n in ("q", "k", "v", "dout"))
+    cu = tr["cu_seqlens"].to(dev)
+    T, h_q, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((h_q, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    vd = attn.varlen_dims(q, k, cu, tr["max_seqlen"])
+    ws = torch.empty(max(attn.bwd_workspace_bytes(vd), 1), dtype=torch.uint8, device=dev)
+    dq_, kp, vp, bt, ctx = (de[n].to(dev) for n in ("q", "k_pool", "v_pool", "block_table",
+                                                    "ctx_lens"))
+    od = torch.empty_like(dq_)
+    pdims = attn.paged_dims(dq_, kp, bt, de["max_ctx"])
+    wsd = torch.empty(max(attn.decode_workspace_bytes(pdims), 1), dtype=torch.uint8, device=dev)
+    scale = tr["scale"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        attn.fwd(q, k, v, cu, scale, o=o, lse=lse, max_seqlen=tr["max_seqlen"])
+        if ev:
+            ev[1].record()
+        attn.bwd(q, k, v, o, lse, dout, cu, scale, dq=dq, dk=dk, dv=dv,
+                 max_seqlen=tr["max_seqlen"], workspace=ws)
+        if ev:
+            ev[2].record()
+        attn.decode_paged(dq_, kp, vp, bt, ctx, de["scale"], o=od, max_ctx_len=de["max_ctx"],
+                          workspace=wsd)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    t_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+
+    f_fwd, f_bwd, b_fwd, b_bwd = train_costs(tr)
+    f_dec, b_dec = decode_costs(de)
+    tflops = (f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12
+    dec_gbps = b_dec / t_dec / 1e9
+
+    parts = {
+        "attn_fwd": dict(t=t_fwd, bound="mfma", achieved=f_fwd / t_fwd / 1e12,
+                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_fwd),
+        "attn_bwd": dict(t=t_bwd, bound="mfma", achieved=f_bwd / t_bwd / 1e12,
+                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_bwd),
+        "attn_decode_paged": dict(t=t_dec, bound="hbm", achieved=dec_gbps, peak=HBM_PEAK_GBPS,
+                                  unit="GB/s", alg=b_dec),
+    }
+    dom = max(parts, key=lambda n: parts[n]["t"])
+    p = parts[dom]
+    roofline = {"kernel": dom, "bound": p["bound"], "achieved": round(p["achieved"], 2),
+                "peak": p["peak"], "unit": p["unit"], "frac": round(p["achieved"] / p["peak"], 4),
+                "traffic": read_traffic(dom)}
+
+    out = {
+        "metric": "attn fwd+bwd TFLOP/s & % FP16 MFMA peak; paged-decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3_train fwd+bwd (B=8, S=1024, H_q=16, H_kv=8, d=128, causal) + "
+                        "paged_decode (256 seqs, ctx U{128..4096}, block 16, H_q=16, H_kv=8, "
+                        "d=128)",
+            "global_batch": 8, "seq_len": 1024, "parallelism": "single-gpu",
+        },
+        "mfma_peak_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "fwd": {"us": round(t_fwd * 1e6, 2), "TFLOP/s": round(parts["attn_fwd"]["achieved"], 2),
+                "GB/s": round(b_fwd / t_fwd / 1e9, 1)},
+        "bwd": {"us": round(t_bwd * 1e6, 2), "TFLOP/s": round(parts["attn_bwd"]["achieved"], 2),
+                "GB/s": round(b_bwd / t_bwd / 1e9, 1), "launches": 3},
+        "decode": {"us": round(t_dec * 1e6, 2), "GB/s": round(dec_gbps, 1),
+                   "hbm_peak_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "alg_bytes": int(b_dec), "launches": 2},
+        "roofline": roofline,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args.cpu_budget)
+        cb.pop("seconds", None)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

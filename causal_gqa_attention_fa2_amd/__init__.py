@@ -17,4 +17,6 @@ from .attn import (  # noqa: F401
     decode_workspace_bytes,
     fwd,
     load_library,
+    paged_dims,
+    varlen_dims,
 )
