@@ -56,14 +56,14 @@ attn_status check_paged(const attn_paged_dims* d, bool* empty) {
   return ATTN_OK;
 }
 
-int decode_max_splits(const attn_paged_dims* d) {
-  return (d->max_ctx_len + cgqa::kDecodeSplit - 1) / cgqa::kDecodeSplit;
-}
-
-size_t decode_ws_parts(const attn_paged_dims* d, size_t* o_bytes) {
-  const size_t slots = (size_t)d->n_seqs * d->h_q * decode_max_splits(d);
+// Workspace of the decode: partial outputs, partial (max, sum) pairs and the
+// work plan (block prefix sums and each work-group's first sequence).
+size_t decode_ws_parts(const attn_paged_dims* d, size_t* o_bytes, size_t* ml_bytes) {
+  const int nwg = cgqa::decode_num_wgs(d->n_seqs, d->max_ctx_len);
+  const size_t slots = (size_t)(nwg + d->n_seqs) * d->h_q;
   *o_bytes = align_up(slots * d->head_dim * sizeof(float));
-  return *o_bytes + align_up(slots * 2 * sizeof(float));
+  *ml_bytes = align_up(slots * 2 * sizeof(float));
+  return *o_bytes + *ml_bytes + align_up((size_t)(d->n_seqs + 1 + nwg) * sizeof(int32_t));
 }
 
 }  // namespace
@@ -159,8 +159,8 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
 size_t attn_decode_workspace_bytes(const attn_paged_dims* dims) {
   bool empty = false;
   if (check_paged(dims, &empty) != ATTN_OK || empty) return 0;
-  size_t ob;
-  return decode_ws_parts(dims, &ob);
+  size_t ob, mb;
+  return decode_ws_parts(dims, &ob, &mb);
 }
 
 attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
@@ -176,8 +176,8 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
   if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
     return ATTN_ERR_INVALID_ARG;
-  size_t ob;
-  const size_t need = decode_ws_parts(dims, &ob);
+  size_t ob, mb;
+  const size_t need = decode_ws_parts(dims, &ob, &mb);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign)))
     return ATTN_ERR_WORKSPACE;
   cgqa::DecodeArgs a;
@@ -189,12 +189,13 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
   a.o = o;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + ob);
+  a.plan = (int32_t*)((char*)workspace + ob + mb);
   a.n_seqs = dims->n_seqs;
   a.h_q = dims->h_q;
   a.h_kv = dims->h_kv;
   a.head_dim = dims->head_dim;
   a.max_blocks_per_seq = dims->max_blocks_per_seq;
-  a.max_splits = decode_max_splits(dims);
+  a.n_wgs = cgqa::decode_num_wgs(dims->n_seqs, dims->max_ctx_len);
   a.scale = scale;
   return cgqa::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -7,18 +7,28 @@
 // work is a gather-and-reduce that reads every context key and value once,
 // so it is bound by HBM bandwidth; it runs on the vector ALUs, not on MFMA.
 //
-// Split-context scheme (two launches):
-//   1. split:   one work-group (4 waves) per (sequence, KV head, 512-token
-//               split). A wave takes every 4th block of the split; in a wave
-//               each token row of a block is held by D/8 lanes with 16 bytes
-//               each, so one load instruction gathers 64 / (D/8) rows. The G
-//               query heads of the KV head share every loaded block.
-//               Each lane keeps an online-softmax state (max, sum, 8 output
-//               columns) per query head; the states are merged across the
-//               lanes' token rows, across waves through LDS, and written as
-//               the split's partial (unnormalised output, max, sum).
-//   2. combine: per (sequence, query head), merge the splits' partials by
-//               their maxima and write fp16 output.
+// Balanced split-context scheme (three launches):
+//   1. plan:    one work-group prefix-sums the block counts ceil(ctx/16) of
+//               the sequences and records, for each gather work-group, the
+//               sequence its range starts in.
+//   2. gather:  the flattened (sequence, block) space is cut into n_wgs equal
+//               contiguous ranges, one per work-group, whatever the mix of
+//               context lengths (ranges may span several sequences). A
+//               work-group has one wave per KV head (up to 8); its waves walk
+//               the same blocks together, so the KV heads of each token row
+//               (one contiguous run of h_kv * d halves) are fetched at the
+//               same time. In a wave each token row of a block is held by D/8
+//               lanes with 16 bytes each; one load instruction gathers
+//               64 / (D/8) rows and two blocks are in flight per wave. The G
+//               query heads of the KV head share every loaded block. q.k and
+//               the P.V sums use v_dot2_f32_f16 (fp16 products, fp32 sums);
+//               row sums of q.k use DPP lane moves. Each lane keeps an
+//               online-softmax state (max, sum, 8 output columns) per query
+//               head; at the end of each sequence segment the lanes' states
+//               are merged and stored as a partial in slot (work-group +
+//               sequence), which is unique because the ranges are ordered.
+//   3. combine: per (sequence, query head), merge the partials of the
+//               work-groups that covered the sequence and write fp16 output.
 #include "cdna4.h"
 #include "kernels.h"
 
@@ -26,6 +36,8 @@ namespace cgqa {
 namespace {
 
 constexpr int kMaxG = 16;
+constexpr int kDecodeWaves = 8;  // KV heads (waves) per gather work-group
+constexpr int kPlanThreads = 1024;
 
 struct DecParams {
   const f16* __restrict__ q;
@@ -36,7 +48,9 @@ struct DecParams {
   f16* __restrict__ o;
   float* __restrict__ part_o;
   float* __restrict__ part_ml;
-  int n, h_q, h_kv, G, max_blocks, max_splits;
+  int32_t* __restrict__ blk_start;  // [n + 1]
+  int32_t* __restrict__ wg_first;   // [n_wgs]
+  int n, h_q, h_kv, G, max_blocks, n_wgs;
   float scale_log2;
 };
 
@@ -55,36 +69,89 @@ __device__ __forceinline__ void merge_state(SoftState& s, float m2, float l2, co
   s.m = M;
 }
 
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of N lanes (N = 8 or 16) with DPP moves; every
+// lane of the group ends with the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8-lane half
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);  // row_mirror: other half of the row
+  return x;
+}
+
+// Two fp16 values (lo from a, hi from b) taken from the same half of two words.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                false);
+}
+
+// Exclusive prefix sum of the sequences' block counts into blk_start[0..n]
+// and, for every gather work-group whose range starts in sequence b,
+// wg_first[w] = b. One work-group.
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecParams p) {
+  __shared__ int32_t part[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int per = ceil_div(p.n, kPlanThreads);
+  const int b0 = min(p.n, tid * per);
+  const int b1 = min(p.n, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += ceil_div(p.ctx[b], 16);
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan
+    const int x = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  const int total = part[kPlanThreads - 1];
+  const int chunk = max(1, ceil_div(total, p.n_wgs));
+  int start = part[tid] - local;
+  for (int b = b0; b < b1; ++b) {
+    const int nb = ceil_div(p.ctx[b], 16);
+    p.blk_start[b] = start;
+    for (int w = ceil_div(start, chunk); w * chunk < start + nb; ++w) p.wg_first[w] = b;
+    start += nb;
+  }
+  if (tid == kPlanThreads - 1) p.blk_start[p.n] = total;
+}
+
+// One wave: online softmax of the G query heads of KV head g of sequence b
+// over its logical blocks [j0, j1); the merged state goes to partial slot
+// `slot`.
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
+__device__ __forceinline__ void gather_segment(const DecParams& p, int b, int g, int j0, int j1,
+                                               int slot, int lane) {
   constexpr int LPR = D / 8;      // lanes per token row
   constexpr int TPI = 64 / LPR;   // token rows per load instruction
   constexpr int NLD = 16 / TPI;   // load instructions per 16-token block
-  __shared__ float xch[4][G][LPR][10];
+  constexpr int NB = 2;           // blocks in flight per wave
+  constexpr int NTOK = NB * NLD;  // tokens per lane per iteration
+  const int rg = lane / LPR;      // token row within a load instruction
+  const int dc = lane % LPR;      // 8-column chunk of the head dimension
+  const int t_end = p.ctx[b];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int ctx = p.ctx[b];
-  const int t_begin = split * kDecodeSplit;
-  if (t_begin >= ctx) return;
-  const int t_end = min(ctx, t_begin + kDecodeSplit);
-  const int blk_begin = t_begin / 16;
-  const int blk_end = (t_end + 15) / 16;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int rg = lane / LPR;  // token row within a load instruction
-  const int dc = lane % LPR;  // 8-column chunk of the head dimension
-
-  float qv[G][8];
+  u32x4 qh[G];  // q chunk of each head as fp16 pairs
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const f16x8 x = *(const f16x8*)(p.q + ((size_t)b * p.h_q + g * G + h) * D + dc * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[h][e] = (float)x[e] * p.scale_log2;
-  }
+  for (int h = 0; h < G; ++h)
+    qh[h] = *(const u32x4*)(p.q + ((size_t)b * p.h_q + g * G + h) * D + dc * 8);
   SoftState st[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -94,56 +161,98 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
     for (int e = 0; e < 8; ++e) st[h].a[e] = 0.f;
   }
 
-  const int32_t* table = p.bt + (size_t)b * p.max_blocks;
   const size_t row_stride = (size_t)p.h_kv * D;  // halves between token rows
-  for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
-    const int phys = table[blk];
-    const f16* kb = p.kp + ((size_t)phys * 16) * row_stride + (size_t)g * D + dc * 8;
-    const f16* vb = p.vp + ((size_t)phys * 16) * row_stride + (size_t)g * D + dc * 8;
-    f16x8 kr[NLD], vr[NLD];
-    bool ok[NLD];
+  const f16* kbase = p.kp + (size_t)g * D + dc * 8;
+  const f16* vbase = p.vp + (size_t)g * D + dc * 8;
+  const int32_t* table = p.bt + (size_t)b * p.max_blocks;
+  for (int win = j0; win < j1; win += 64) {
+    // Table entries of the next (up to) 64 blocks, one per lane.
+    const int cnt = min(64, j1 - win);
+    int my_phys = 0;
+    if (lane < cnt) my_phys = table[win + lane];
+    for (int i0 = 0; i0 < cnt; i0 += NB) {
+      // Loads are unconditional (a guarded load lets the compiler reuse its
+      // destination register and wait on it before issuing the next one):
+      // rows past the context read the block's unused slots and are masked
+      // below; a missing second block re-reads the first.
+      u32x4 kr[NTOK], vr[NTOK];
+      bool ok[NTOK];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int tok = j * TPI + rg;
-      ok[j] = blk * 16 + tok < t_end;
-      kr[j] = zero_f16x8();
-      vr[j] = zero_f16x8();
-      if (ok[j]) {
-        kr[j] = *(const f16x8*)(kb + (size_t)tok * row_stride);
-        vr[j] = *(const f16x8*)(vb + (size_t)tok * row_stride);
+      for (int bb = 0; bb < NB; ++bb) {
+        const int i = i0 + bb;
+        const int phys = __builtin_amdgcn_readlane(my_phys, i < cnt ? i : i0);
+        const size_t base = (size_t)phys * 16 * row_stride;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const int tok = j * TPI + rg;
+          const int t = bb * NLD + j;
+          ok[t] = i < cnt && (win + i) * 16 + tok < t_end;
+          kr[t] = *(const u32x4*)(kbase + base + (size_t)tok * row_stride);
+          vr[t] = *(const u32x4*)(vbase + base + (size_t)tok * row_stride);
+        }
       }
-    }
+      // Keep every load of the iteration ahead of the arithmetic that uses it.
+      __builtin_amdgcn_sched_barrier(0);
+      // Masked rows may hold anything (even NaN): zero their values.
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s[NLD];
-      float mx = kMaxInit;
+      for (int t = 0; t < NTOK; ++t) {
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += qv[h][e] * (float)kr[j][e];
-#pragma unroll
-        for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
-        s[j] = ok[j] ? acc : -INFINITY;
-        mx = fmaxf(mx, s[j]);
+        for (int c = 0; c < 4; ++c) vr[t][c] = ok[t] ? vr[t][c] : 0u;
       }
-      const float m_new = fmaxf(st[h].m, mx);
-      const float alpha = fast_exp2(st[h].m - m_new);
-      st[h].m = m_new;
-      st[h].l *= alpha;
+      // Values of token pairs (2u, 2u+1) interleaved per column for v_dot2.
+      u32x4 vlo[NTOK / 2], vhi[NTOK / 2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st[h].a[e] *= alpha;
+      for (int u = 0; u < NTOK / 2; ++u) {
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const float pj = fast_exp2(s[j] - m_new);
-        st[h].l += pj;
+        for (int c = 0; c < 4; ++c) {
+          vlo[u][c] = pair_lo(vr[2 * u][c], vr[2 * u + 1][c]);
+          vhi[u][c] = pair_hi(vr[2 * u][c], vr[2 * u + 1][c]);
+        }
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st[h].a[e] += pj * (float)vr[j][e];
+      for (int h = 0; h < G; ++h) {
+        float s[NTOK];
+        float mx = kMaxInit;
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+          float acc = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc = fdot2(kr[t][c], qh[h][c], acc);
+          acc = group_sum<LPR>(acc) * p.scale_log2;
+          s[t] = ok[t] ? acc : -INFINITY;
+          mx = fmaxf(mx, s[t]);
+        }
+        const float m_new = fmaxf(st[h].m, mx);
+        const float alpha = fast_exp2(st[h].m - m_new);
+        st[h].m = m_new;
+        float lsum = 0.f;
+        uint32_t pp[NTOK / 2];
+#pragma unroll
+        for (int u = 0; u < NTOK / 2; ++u) {
+          const f16 p0 = (f16)fast_exp2(s[2 * u] - m_new);
+          const f16 p1 = (f16)fast_exp2(s[2 * u + 1] - m_new);
+          lsum += (float)p0 + (float)p1;
+          pp[u] = __builtin_bit_cast(uint32_t, f16x2{p0, p1});
+        }
+        st[h].l = st[h].l * alpha + lsum;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float a0 = st[h].a[2 * c] * alpha;
+          float a1 = st[h].a[2 * c + 1] * alpha;
+#pragma unroll
+          for (int u = 0; u < NTOK / 2; ++u) {
+            a0 = fdot2(vlo[u][c], pp[u], a0);
+            a1 = fdot2(vhi[u][c], pp[u], a1);
+          }
+          st[h].a[2 * c] = a0;
+          st[h].a[2 * c + 1] = a1;
+        }
       }
     }
   }
 
-  // Merge the TPI token rows of the wave (lanes dc, dc + LPR, ...).
+  // Merge the TPI token rows of the wave (lanes dc, dc + LPR, ...) and store
+  // the partial from the lanes of row group 0.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -156,36 +265,41 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecParams p) {
       merge_state(st[h], m2, l2, a2);
     }
     if (rg == 0) {
-      xch[wave][h][dc][0] = st[h].m;
-      xch[wave][h][dc][1] = st[h].l;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xch[wave][h][dc][2 + e] = st[h].a[e];
-    }
-  }
-  __syncthreads();
-  // Threads (h, dc) of the first G * LPR merge the four waves.
-  if (tid < G * LPR) {
-    const int h = tid / LPR;
-    const int c = tid % LPR;
-    SoftState s;
-    s.m = xch[0][h][c][0];
-    s.l = xch[0][h][c][1];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s.a[e] = xch[0][h][c][2 + e];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) merge_state(s, xch[w][h][c][0], xch[w][h][c][1], &xch[w][h][c][2]);
-    const size_t slot = ((size_t)b * p.h_q + g * G + h) * p.max_splits + split;
-    float* po = p.part_o + slot * D + c * 8;
-    *(f32x4*)po = f32x4{s.a[0], s.a[1], s.a[2], s.a[3]};
-    *(f32x4*)(po + 4) = f32x4{s.a[4], s.a[5], s.a[6], s.a[7]};
-    if (c == 0) {
-      p.part_ml[2 * slot] = s.m;
-      p.part_ml[2 * slot + 1] = s.l;
+      const size_t row = (size_t)slot * p.h_q + g * G + h;
+      float* po = p.part_o + row * D + dc * 8;
+      *(f32x4*)po = f32x4{st[h].a[0], st[h].a[1], st[h].a[2], st[h].a[3]};
+      *(f32x4*)(po + 4) = f32x4{st[h].a[4], st[h].a[5], st[h].a[6], st[h].a[7]};
+      if (dc == 0) {
+        p.part_ml[2 * row] = st[h].m;
+        p.part_ml[2 * row + 1] = st[h].l;
+      }
     }
   }
 }
 
-// One wave per (sequence, query head): merge the splits, normalise, store.
+template <int D, int G>
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_gather_kernel(DecParams p) {
+  const int w = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.y * kDecodeWaves + wave;  // KV head of this wave
+  const int total = p.blk_start[p.n];
+  const int chunk = max(1, ceil_div(total, p.n_wgs));
+  int c = w * chunk;
+  const int c_end = min(total, c + chunk);
+  if (c >= c_end || g >= p.h_kv) return;  // no barrier follows: waves may leave
+  int b = p.wg_first[w];
+  while (c < c_end) {
+    const int sb = p.blk_start[b];
+    const int seg_end = min(c_end, p.blk_start[b + 1]);
+    if (seg_end > c) gather_segment<D, G>(p, b, g, c - sb, seg_end - sb, w + b, lane);
+    c = max(c, seg_end);
+    ++b;
+  }
+}
+
+// One wave per (sequence, query head): merge the partials of the work-groups
+// that covered the sequence, normalise, store fp16.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p) {
   constexpr int PER = D / 64;  // output columns per lane
@@ -193,24 +307,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p) {
   const int lane = threadIdx.x & 63;
   if (row >= p.n * p.h_q) return;
   const int b = row / p.h_q;
-  const int ctx = p.ctx[b];
-  const int ns = (ctx + kDecodeSplit - 1) / kDecodeSplit;
+  const int head = row - b * p.h_q;
   f16* out = p.o + (size_t)row * D + lane * PER;
-  if (ns == 0) {
+  const int sb = p.blk_start[b];
+  const int eb = p.blk_start[b + 1];
+  if (eb == sb) {  // empty context
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = (f16)0.f;
     return;
   }
-  const float* ml = p.part_ml + (size_t)row * p.max_splits * 2;
+  const int chunk = max(1, ceil_div(p.blk_start[p.n], p.n_wgs));
+  const int w0 = sb / chunk;
+  const int w1 = (eb - 1) / chunk;
   float M = kMaxInit;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int w = w0; w <= w1; ++w) M = fmaxf(M, p.part_ml[2 * ((size_t)(w + b) * p.h_q + head)]);
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float c = fast_exp2(ml[2 * s] - M);
-    l += ml[2 * s + 1] * c;
-    const float* po = p.part_o + ((size_t)row * p.max_splits + s) * D + lane * PER;
+  for (int w = w0; w <= w1; ++w) {
+    const size_t srow = (size_t)(w + b) * p.h_q + head;
+    const float c = fast_exp2(p.part_ml[2 * srow] - M);
+    l += p.part_ml[2 * srow + 1] * c;
+    const float* po = p.part_o + srow * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] += po[e] * c;
   }
@@ -221,11 +339,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p) {
 
 template <int D>
 hipError_t launch_d(const DecParams& p, int G, hipStream_t stream) {
-  const dim3 grid(p.max_splits, p.h_kv, p.n);
-  // With every context empty there is nothing to gather; combine writes zeros.
-  if (p.max_splits > 0) switch (G) {
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  const int waves = p.h_kv < kDecodeWaves ? p.h_kv : kDecodeWaves;
+  const dim3 grid(p.n_wgs, (p.h_kv + kDecodeWaves - 1) / kDecodeWaves);
+  const dim3 block(64 * waves);
+  switch (G) {
 #define CGQA_G(GG) \
-  case GG: hipLaunchKernelGGL((decode_split_kernel<D, GG>), grid, dim3(256), 0, stream, p); break;
+  case GG: hipLaunchKernelGGL((decode_gather_kernel<D, GG>), grid, block, 0, stream, p); break;
     CGQA_G(1) CGQA_G(2) CGQA_G(3) CGQA_G(4) CGQA_G(5) CGQA_G(6) CGQA_G(7) CGQA_G(8)
     CGQA_G(9) CGQA_G(10) CGQA_G(11) CGQA_G(12) CGQA_G(13) CGQA_G(14) CGQA_G(15) CGQA_G(16)
 #undef CGQA_G
@@ -248,12 +368,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.o = (f16*)a.o;
   p.part_o = a.part_o;
   p.part_ml = a.part_ml;
+  p.blk_start = a.plan;
+  p.wg_first = a.plan + a.n_seqs + 1;
   p.n = a.n_seqs;
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
   p.G = a.h_q / a.h_kv;
   p.max_blocks = a.max_blocks_per_seq;
-  p.max_splits = a.max_splits;
+  p.n_wgs = a.n_wgs;
   p.scale_log2 = a.scale * kLog2e;
   if (p.G > kMaxG) return hipErrorInvalidValue;
   return a.head_dim == 128 ? launch_d<128>(p, p.G, stream) : launch_d<64>(p, p.G, stream);

@@ -43,14 +43,21 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   void* o;
-  float* part_o;   // workspace: fp32 [n, h_q, max_splits, d]
-  float* part_ml;  // workspace: fp32 [n, h_q, max_splits, 2] (max, sum)
-  int n_seqs, h_q, h_kv, head_dim, max_blocks_per_seq, max_splits;
+  float* part_o;   // workspace: fp32 [n_wgs + n, h_q, d] partial outputs
+  float* part_ml;  // workspace: fp32 [n_wgs + n, h_q, 2] partial (max, sum)
+  int32_t* plan;   // workspace: int32 [n + 1] block prefix sums, [n_wgs] first sequences
+  int n_seqs, h_q, h_kv, head_dim, max_blocks_per_seq, n_wgs;
   float scale;
 };
 
-// Tokens of context handled by one decode work-group (a multiple of 16).
-constexpr int kDecodeSplit = 512;
+// Work-groups of the paged-decode gather: the flattened (sequence, block)
+// space is cut into n_wgs equal contiguous ranges. Bounded by the number of
+// blocks any batch with these dims can hold.
+constexpr int kDecodeMaxWGs = 512;
+inline int decode_num_wgs(int n_seqs, int max_ctx_len) {
+  const long long bound = (long long)n_seqs * ((max_ctx_len + 15) / 16);
+  return bound < 1 ? 1 : (bound < kDecodeMaxWGs ? (int)bound : kDecodeMaxWGs);
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

@@ -97,9 +97,13 @@ def test_bwd_workspace(lib):
 def test_decode_argument_checks(lib):
     dims = PagedDims(4, 16, 8, 128, 16, 256, 1000, 4096)
     need = lib.attn_decode_workspace_bytes(ctypes.byref(dims))
-    splits = 4096 // 512
-    slots = 4 * 16 * splits
-    assert need == (slots * 128 * 4 + 255) // 256 * 256 + (slots * 2 * 4 + 255) // 256 * 256
+    nwg = min(512, 4 * (4096 // 16))  # work-groups of the balanced gather
+    slots = (nwg + 4) * 16
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    assert need == al(slots * 128 * 4) + al(slots * 2 * 4) + al((4 + 1 + nwg) * 4)
     p = ctypes.c_void_p
 
     def call(d, ws=FAKE, nbytes=None, q=FAKE, bt=FAKE):
