@@ -32,11 +32,9 @@ attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
   return ATTN_OK;
 }
 
-size_t bwd_ws_parts(const attn_varlen_dims* d, size_t* acc_bytes) {
-  const size_t acc = (size_t)d->total_tokens * d->h_q * d->head_dim * sizeof(float);
-  const size_t row = (size_t)d->h_q * d->total_tokens * sizeof(float);
-  *acc_bytes = align_up(acc);
-  return align_up(acc) + align_up(row);
+// Workspace of the backward: the fp32 row terms D = rowsum(dO * O) [h_q, T].
+size_t bwd_ws_bytes(const attn_varlen_dims* d) {
+  return align_up((size_t)d->h_q * d->total_tokens * sizeof(float));
 }
 
 attn_status check_paged(const attn_paged_dims* d, bool* empty) {
@@ -111,8 +109,7 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
 size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims) {
   bool empty = false;
   if (check_varlen(dims, &empty) != ATTN_OK || empty) return 0;
-  size_t acc;
-  return bwd_ws_parts(dims, &acc);
+  return bwd_ws_bytes(dims);
 }
 
 attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k, const void* v,
@@ -129,8 +126,7 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       ((uintptr_t)cu_seqlens & 3u))
     return ATTN_ERR_INVALID_ARG;
-  size_t acc_bytes;
-  const size_t need = bwd_ws_parts(dims, &acc_bytes);
+  const size_t need = bwd_ws_bytes(dims);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign))
     return ATTN_ERR_WORKSPACE;
   cgqa::BwdArgs a;
@@ -144,8 +140,7 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dq_acc = (float*)workspace;
-  a.drow = (float*)((char*)workspace + acc_bytes);
+  a.drow = (float*)workspace;
   a.n_seqs = dims->n_seqs;
   a.total_tokens = dims->total_tokens;
   a.max_seqlen = dims->max_seqlen;

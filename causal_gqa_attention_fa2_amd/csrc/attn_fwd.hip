@@ -9,15 +9,21 @@
 // LSE = m + ln l for the backward pass. FP16 inputs, FP32 accumulation
 // (pitchhut "Key Features", item 1).
 //
-// Work decomposition. One work-group of at most four waves per (sequence,
-// query tile, KV head, head chunk). A chunk holds hpw = min(G, 4) of the
-// G = h_q / h_kv query heads of the KV head and the query tile
-// BR = 32 * nqb positions (nqb = 4 / hpw), one 64-lane wave per (head, 32
-// positions). For G <= 4 there is one chunk, so every K/V tile is read from
-// HBM once per KV head and shared by all G heads through LDS
-// (grouped-query sharing).
+// Work decomposition. One work-group of eight waves per (sequence, query
+// tile, KV head, head chunk): hpw heads of the KV head's group times
+// 32 * 8 / hpw query positions, one wave per (head, 32 positions). For the
+// usual group sizes (1, 2, 4, 8) there is one chunk, so every K/V tile is
+// read from HBM once per KV head and shared by all G heads through LDS
+// (grouped-query sharing); eight waves (two per SIMD) share each tile.
 //
-// Per wave and 64-key tile, everything stays in registers:
+// K/V tiles of 64 keys pass through a three-stage LDS ring filled by direct
+// global-to-LDS copies (no staging registers): the copies of tile t+2 are
+// issued right after the barrier that opens tile t, so they have the compute
+// of tiles t and t+1 to arrive; one barrier per tile. K is stored with the
+// row-read chunk swizzle and V with the transpose-read swizzle (cdna4.h), so
+// both operand loads are free of bank conflicts.
+//
+// Per wave and tile, everything else stays in registers:
 //   S^T = K Q^T      32x32x16 MFMA; K from LDS (rows = keys), Q^T from
 //                    registers. In the accumulator layout lane l owns query
 //                    column l % 32, so a row's max and sum are an in-lane
@@ -26,13 +32,19 @@
 //   O^T += V^T P^T   32x32x16 MFMA; P^T feeds the B operand straight from
 //                    the S^T accumulators; V^T is read from the row-major V
 //                    tile with ds_read_b64_tr_b16.
+// The O rescale is skipped when no row maximum of the wave grew (alpha = 1).
 #include "cdna4.h"
 #include "kernels.h"
+
+#include <type_traits>
+
 
 namespace cgqa {
 namespace {
 
-constexpr int kBC = 64;  // keys per tile
+constexpr int kBC = 64;                // keys per tile
+constexpr int kStages = 3;             // LDS ring depth
+constexpr int kNTH = 64 * kQWaves;     // threads per work-group
 
 struct FwdParams {
   const f16* __restrict__ q;
@@ -46,13 +58,17 @@ struct FwdParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  constexpr int KP = D + 8;   // K tile row pitch (halves): natural 16-byte reads
-  constexpr int VP = D + 16;  // V tile row pitch (halves): transpose reads
-  constexpr int NT = D / 16;  // MFMA k-steps over the head dimension
-  constexpr int ND = D / 32;  // 32-wide output blocks over the head dimension
-  __shared__ __attribute__((aligned(16))) f16 Ks[kBC * KP];
-  __shared__ __attribute__((aligned(16))) f16 Vs[kBC * VP];
+__global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
+  constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CH; // tile rows per copy instruction
+  constexpr int IPW = kBC * CH / 64 / kQWaves;  // copy instructions per wave per tensor
+  static_assert(IPW >= 1 && kBC * CH == 64 * kQWaves * IPW, "tile must split over the waves");
+  // K (row reads, chunk swizzle) and V (transpose reads, transpose swizzle)
+  // tiles, unpadded so that the direct copies fill them in lane order.
+  __shared__ __attribute__((aligned(16))) f16 Ks[kStages][kBC * D];
+  __shared__ __attribute__((aligned(16))) f16 Vs[kStages][kBC * D];
 
   const int BR = 32 * p.nqb;
   // Heaviest query tiles (the last ones of the longest sequences) first.
@@ -77,121 +93,147 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int grp = lane >> 4;
   const int j16 = lane & 15;
   const int hig = chunk * p.hpw + wave / p.nqb;  // head within the group
-  const int head = g * p.G + hig;
+  const int head = g * p.G + min(hig, p.G - 1);
   const int q0 = q_wg0 + (wave % p.nqb) * 32;
   const int qpos = q0 + l32;
+  const bool wave_has_rows = q0 < L && hig < p.G;
   const bool qvalid = qpos < L && hig < p.G;
 
-  // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7].
+  // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7]. Rows past the
+  // sequence read its last row (loads stay unconditional) and are never stored.
   f16x8 qf[NT];
   {
-    const f16* qrow = p.q + ((size_t)(s0 + qpos) * p.h_q + head) * D + 8 * hi;
+    const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) qf[t] = zero_f16x8();
-    if (qvalid) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
-    }
+    for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
   }
+
+  // Copy of K/V tile kt into ring stage `stage`: instruction i of this wave
+  // fills rows (wave * IPW + i) * RPI + lane / CH; lane l lands in chunk slot
+  // l % CH of its row and fetches the global chunk that the swizzle maps
+  // there. Keys past the sequence fetch its last row: their scores are
+  // masked and their weights are zero.
+  auto issue_tile = [&](int kt, int stage) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (wave * IPW + i) * RPI + lane / CH;
+      const int slot = (lane % CH) * 8;
+      const size_t row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
+      f16* kdst = Ks[stage] + (wave * IPW + i) * 64 * 8;
+      f16* vdst = Vs[stage] + (wave * IPW + i) * 64 * 8;
+      dma16(p.k + row + swz<D>(r, slot), kdst);
+      dma16(p.v + row + swz_tr<D>(r, slot), vdst);
+    }
+  };
 
   f32x16 oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = zero_f32x16();
-  float m_run = kMaxInit;
-  float l_run = 0.f;  // this half-wave's share of the row sum
+  float m_run = kMaxInit;  // running max of the scaled scores (log2 units)
+  float l_run = 0.f;       // this half-wave's share of the row sum
 
-  const int nthreads = blockDim.x;
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  const bool wave_has_rows = q0 < L && hig < p.G;
+  // Per-lane LDS offsets (halves) of the operand reads, fixed for the whole
+  // loop: the chunk swizzles depend on the row only through row % 16 (K) and
+  // row % 4 (V), so the other rows of a lane's reads sit at constant
+  // distances and every read below is base + per-lane offset + immediate.
+  int koff[NT];  // K row l32, columns 16t + 8hi (row 32 + l32: + 32 D)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) koff[t] = l32 * D + swz<D>(l32, 16 * t + 8 * hi);
+  int voff[ND];  // V rows 4hi + j16/4 (+ 16u, + 8), columns 32db + 16(grp&1) + 4(j16&3)
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    const int r = 4 * hi + (j16 >> 2);
+    voff[db] = r * D + swz_tr<D>(r, 32 * db + 16 * (grp & 1) + 4 * (j16 & 3));
+  }
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    for (int c = tid; c < kBC * CH; c += nthreads) {
-      const int r = c / CH;
-      const int cc = c - r * CH;
-      const int key = kt * kBC + r;
-      f16x8 kv = zero_f16x8(), vv = zero_f16x8();
-      if (key < L) {
-        const size_t off = ((size_t)(s0 + key) * p.h_kv + g) * D + cc * 8;
-        kv = *(const f16x8*)(p.k + off);
-        vv = *(const f16x8*)(p.v + off);
-      }
-      *(f16x8*)(Ks + r * KP + cc * 8) = kv;
-      *(f16x8*)(Vs + r * VP + cc * 8) = vv;
+  // One tile step on ring stage S = kt % 3 (a compile-time constant); the
+  // copies of tile kt + 2 go to stage (S + 2) % 3, which held tile kt - 1.
+  auto step = [&](int kt, auto S) {
+    constexpr int stage = decltype(S)::value;
+    // Tile kt has landed (this wave's copies; tile kt + 1's may still fly),
+    // then every wave's copies have, and every wave is done with tile kt - 1.
+    if (kt + 1 < n_kt) wait_vm_barrier<2 * IPW>();
+    else wait_vm_barrier<0>();
+    if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % kStages);
+
+    if (!wave_has_rows || kt * kBC > q0 + 31) return;  // fully masked for this wave
+    const f16* Kb = Ks[stage];
+    const f16* Vb = Vs[stage];
+    // S^T for the two 32-key halves of the tile, as two interleaved chains.
+    f32x16 s[2] = {zero_f32x16(), zero_f32x16()};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[0] = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], s[0]);
+      s[1] = mfma32x32x16(*(const f16x8*)(Kb + 32 * D + koff[t]), qf[t], s[1]);
     }
-    __syncthreads();
-    if (!wave_has_rows || kt * kBC > q0 + 31) continue;  // tile fully masked for this wave
-
-    // S^T for the two 32-key halves of the tile.
-    f32x16 s[2];
+    // Causal mask (diagonal tiles only) and the tile maximum of raw scores.
+    if (kt * kBC + kBC - 1 > q0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero_f32x16();
-      const f16* krow = Ks + (kb * 32 + l32) * KP + 8 * hi;
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s[kb] = mfma32x32x16(*(const f16x8*)(krow + 16 * t), qf[t], s[kb]);
-    }
-
-    // Scale into log2 units, causal mask, tile maximum.
-    const bool need_mask = kt * kBC + kBC - 1 > q0;
-    float mx = kMaxInit;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * p.scale_log2;
-        if (need_mask) {
+        for (int i = 0; i < 16; ++i) {
           const int key = kt * kBC + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key > qpos) x = -INFINITY;
+          if (key > qpos) s[kb][i] = -INFINITY;
         }
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
       }
     }
-    mx = half_swap_max(mx);
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    mx = half_swap_max(mx) * p.scale_log2;
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
+    // Rescale only when some row's maximum grew (alpha == 1 otherwise).
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+    }
     m_run = m_new;
 
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(s[kb][i] - m_new);
-        s[kb][i] = e;
-        rs += e;
-      }
-    }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-
-    // P^T as B operands: k-step u covers tile keys 16u..16u+15; slot s of
-    // half hi holds key 16u + 8(s/4) + 4hi + s%4.
+    // P^T = exp2(S^T * scale * log2(e) - m), as B operands: k-step u covers
+    // tile keys 16u..16u+15; slot e of half hi holds key 16u + 8(e/4) +
+    // 4hi + e%4.
     f16x8 pf[4];
+    float rs = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[u][e] = (f16)s[u >> 1][8 * (u & 1) + e];
+      for (int e = 0; e < 8; ++e) {
+        const float x = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + e], p.scale_log2, -m_new));
+        rs += x;
+        pf[u][e] = (f16)x;
+      }
     }
+    l_run += rs;
 
-    // O^T += V^T P^T. A operand slot s of half hi must hold V[key(s)][d]
-    // for the same keys: two transpose reads of 4 rows each.
+    // O^T += V^T P^T. A-operand slot e of half hi must hold V[key(e)][d]
+    // for the same keys: transpose reads of rows 16u + 4hi + j16/4 and 8
+    // rows further.
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      const int dcol = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int krow = 16 * u + 4 * hi + (j16 >> 2);
-        const f16x4 lo = lds_read_tr(Vs + krow * VP + dcol);
-        const f16x4 up = lds_read_tr(Vs + (krow + 8) * VP + dcol);
+        const f16x4 lo = lds_read_tr(Vb + voff[db] + 16 * u * D);
+        const f16x4 up = lds_read_tr(Vb + voff[db] + (16 * u + 8) * D);
         oacc[db] = mfma32x32x16(cat4(lo, up), pf[u], oacc[db]);
       }
     }
+  };
+
+  // Q^T was loaded with ordinary loads: wait for them here with the builtin
+  // (whose effect the compiler tracks), so it places no wait of its own inside
+  // the loop, where such a wait would also stall on the copies in flight.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  issue_tile(0, 0);
+  if (n_kt > 1) issue_tile(1, 1);
+  for (int kt = 0; kt < n_kt; kt += kStages) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
   }
 
   const float l_tot = half_swap_sum(l_run);  // all lanes take part in the exchange
@@ -226,18 +268,18 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
   p.G = a.h_q / a.h_kv;
-  p.hpw = p.G < 4 ? p.G : 4;
-  p.nqb = 4 / p.hpw;
-  p.n_chunks = (p.G + p.hpw - 1) / p.hpw;
+  const QTileLayout lay = qtile_layout(p.G);
+  p.hpw = lay.hpw;
+  p.nqb = lay.nqb;
+  p.n_chunks = lay.n_chunks;
   const int BR = 32 * p.nqb;
   p.n_qtiles = (a.max_seqlen + BR - 1) / BR;
   p.scale_log2 = a.scale * kLog2e;
   const dim3 grid(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
-  const dim3 block(64 * p.hpw * p.nqb);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(kNTH), 0, stream, p);
   else
-    hipLaunchKernelGGL(fwd_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(kNTH), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -64,6 +64,61 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ f16x8 zero_f16x8() { return f16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
 
+// Column (in halves) of element (row, col) in an LDS tile of D-half rows with
+// no padding whose 16-byte chunks are XOR-swizzled per row, for tiles read
+// both ways by the MFMA operand loads. With D = 128 on the 64-bank LDS,
+// 16-byte row reads of 16 consecutive rows hit 16 distinct chunk slots, and
+// ds_read_b64_tr_b16 over 4 consecutive rows (row % 4 == 0) by two 16-lane
+// groups 32 bytes apart hits 8 distinct 32-byte slots (measured on gfx950:
+// row reads at the conflict-free rate, transpose reads at ~80% of the rate of
+// a 160-half padded tile). `col` may be any multiple of 4.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  const int f = D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+  return (((col >> 3) ^ f) << 3) | (col & 7);
+}
+
+// Column of element (row, col) in an unpadded D-half LDS tile read only by
+// ds_read_b64_tr_b16 (4 consecutive rows, row % 4 == 0, two 16-lane groups
+// 32 bytes apart): the 16-byte chunks of row r are XOR-ed with 4 * (r % 4),
+// which keeps every 32-byte pair in order and spreads the 8 pairs of a pass
+// over all 64 banks (measured on gfx950 at the rate of a 160-half padded
+// tile).
+template <int D>
+__device__ __forceinline__ int swz_tr(int row, int col) {
+  const int f = D == 128 ? ((row & 3) << 2) : (((row & 3) << 1) & 7);
+  return (((col >> 3) ^ f) << 3) | (col & 7);
+}
+
+// Asynchronous 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's 16 bytes land at lds_wave_base + 16 l,
+// so one wave fills 1 KB of LDS in lane order; lds_wave_base must be the same
+// for every lane of the wave. Completion is tracked by vmcnt, like an
+// ordinary load. The copy is issued from inline assembly so the compiler's
+// wait insertion does not see it: otherwise it cannot tell the ring stage
+// being read from the stages still being filled and waits for every copy in
+// flight before each LDS read. The caller therefore owns the waits
+// (wait_vm_barrier) and must not issue other vector-memory loads whose
+// completion the compiler would track while copies are in flight. M0 holds
+// the LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, f16* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// and all its LDS operations are done, then barrier. No memory fence is
+// emitted (a fence would also wait for the copies still meant to be in
+// flight); the asm memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ f32x16 zero_f32x16() {
   f32x16 z;
 #pragma unroll

@@ -30,7 +30,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // workspace: fp32 [T, h_q, d]
   float* drow;    // workspace: fp32 [h_q, T], rowsum(dO * O)
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   float scale;
@@ -57,6 +56,21 @@ constexpr int kDecodeMaxWGs = 512;
 inline int decode_num_wgs(int n_seqs, int max_ctx_len) {
   const long long bound = (long long)n_seqs * ((max_ctx_len + 15) / 16);
   return bound < 1 ? 1 : (bound < kDecodeMaxWGs ? (int)bound : kDecodeMaxWGs);
+}
+
+// Query-stationary work-groups (forward and dQ) have kQWaves waves; each wave
+// owns 32 query rows of one head. A work-group covers hpw heads of a KV
+// group (hpw = the largest power of two <= min(G, kQWaves)) and
+// 32 * kQWaves / hpw query positions; a group of G heads needs
+// ceil(G / hpw) head chunks.
+constexpr int kQWaves = 8;
+struct QTileLayout {
+  int hpw, nqb, n_chunks;
+};
+inline QTileLayout qtile_layout(int G) {
+  int hpw = 1;
+  while (hpw * 2 <= G && hpw * 2 <= kQWaves) hpw *= 2;
+  return QTileLayout{hpw, kQWaves / hpw, (G + hpw - 1) / hpw};
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

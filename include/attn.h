@@ -106,8 +106,7 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
                      float* lse, void* stream);
 
 /* Bytes of device workspace attn_bwd needs for `dims` (0 for an empty
- * batch). Holds an fp32 dQ accumulator [T, h_q, d] and the fp32 row terms
- * D = rowsum(dO * O) [h_q, T]. */
+ * batch). Holds the fp32 row terms D = rowsum(dO * O) [h_q, T]. */
 size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims);
 
 /*
@@ -123,7 +122,8 @@ size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims);
  *                                 query heads
  *   workspace  device buffer of at least attn_bwd_workspace_bytes(dims)
  *              bytes, 256-byte aligned; the library initialises it.
- * dq accumulates with fp32 atomics, so its low bits may differ run to run.
+ * No atomics are used: dq, dk and dv are bitwise reproducible for identical
+ * inputs.
  */
 attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
                      const void* v, const void* o, const float* lse, const void* dO,
@@ -131,7 +131,8 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_decode_paged needs for `dims`: fp32
- * per-split partial outputs, maxima and sums. */
+ * partial outputs, maxima and sums of the context splits, and the int32 work
+ * plan (per-sequence block offsets). The library initialises it. */
 size_t attn_decode_workspace_bytes(const attn_paged_dims* dims);
 
 /*
@@ -149,7 +150,8 @@ size_t attn_decode_workspace_bytes(const attn_paged_dims* dims);
  *   scale       multiplies q.k (usually 1/sqrt(d))
  *   workspace   at least attn_decode_workspace_bytes(dims) bytes
  * Position t of sequence b is slot t % 16 of block block_table[b][t / 16].
- * Pool slots past a sequence's context are never read.
+ * Blocks past ceil(ctx/16) are never read; slots past the context inside the
+ * last block may be read but never influence o (even if they hold NaN).
  */
 attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
                               const void* v_pool, const int32_t* block_table,
