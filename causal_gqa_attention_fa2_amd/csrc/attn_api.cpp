@@ -32,10 +32,12 @@ attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
   return ATTN_OK;
 }
 
-// Workspace of the backward: the fp32 row terms D = rowsum(dO * O) [h_q, T].
-size_t bwd_ws_bytes(const attn_varlen_dims* d) {
+// Workspace of the backward: two fp32 [h_q, T] row-term arrays, D =
+// rowsum(dO * O) and LSE * log2(e), each starting on a 256-byte boundary.
+size_t bwd_row_bytes(const attn_varlen_dims* d) {
   return align_up((size_t)d->h_q * d->total_tokens * sizeof(float));
 }
+size_t bwd_ws_bytes(const attn_varlen_dims* d) { return 2 * bwd_row_bytes(d); }
 
 attn_status check_paged(const attn_paged_dims* d, bool* empty) {
   if (!d) return ATTN_ERR_INVALID_ARG;
@@ -141,6 +143,7 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.dk = dk;
   a.dv = dv;
   a.drow = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + bwd_row_bytes(dims));
   a.n_seqs = dims->n_seqs;
   a.total_tokens = dims->total_tokens;
   a.max_seqlen = dims->max_seqlen;

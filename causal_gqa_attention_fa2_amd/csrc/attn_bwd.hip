@@ -9,37 +9,46 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Two kernels on one stream, no atomics, bitwise reproducible:
-//   1. dq:   query-stationary, shaped like the forward. One work-group per
-//            (sequence, query tile, KV head, head chunk); per wave 32 query
-//            rows of one head. The wave first forms its rows' D from dO and
-//            O (and stores it for kernel 2), then streams K/V tiles through a
-//            double-buffered LDS ring: S^T = K Q^T and dP^T = V dO^T (lane =
-//            query column, so LSE and D are per-lane scalars), dS^T, and
-//            dQ^T += K^T dS^T with K^T taken by transpose reads of the same
-//            K tile. dq is written once, in fp16.
-//   2. dkdv: key-stationary. One work-group per (sequence, 128-key tile, KV
-//            head), four waves of 32 keys; K and V of the wave stay in
-//            registers while the (G query heads) x (32-row query blocks at or
-//            after the keys) stream through a double-buffered LDS ring:
-//            S = Q K^T, dP = dO V^T (lane = key), P and dS, then
-//            dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T by transpose
-//            reads. The G heads of the group add into the same registers.
+//   1. dq:   query-stationary, shaped like the forward. One work-group of
+//            eight waves per (sequence, query tile, KV head, head chunk):
+//            four (head, 32-row query block) slots times two 32-key halves
+//            of each 64-key K/V tile. A wave forms its rows' D from dO and O
+//            (and stores D and LSE * log2(e) for kernel 2), then for every
+//            tile computes, on its key half, S^T = K Q^T and dP^T = V dO^T
+//            (lane = query column, so LSE and D are per-lane scalars), dS^T,
+//            and dQ^T += K^T dS^T with K^T taken by transpose reads of the
+//            same K tile. The two key halves add their partial dQ^T through
+//            LDS at the end; dq is written once, in fp16.
+//   2. dkdv: key-stationary. One work-group of eight waves per (sequence,
+//            128-key tile, KV head); waves w and w + 4 own the same 32 keys.
+//            The (G query heads) x (32-row query blocks at or after the keys)
+//            stream through an LDS ring. Wave w (K in registers) forms
+//            S = Q K^T and P, hands P to wave w + 4 through LDS and adds
+//            dV^T += dO^T P; wave w + 4 (V in registers) works one block
+//            behind: dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS. Each
+//            wave keeps one 32 x d accumulator, so two waves fit per SIMD and
+//            one's matrix work overlaps the other's softmax arithmetic.
 // Compared with a single key-stationary kernel that adds dQ with fp32
 // atomics, this recomputes S and dP once more (7 instead of 5 GEMMs of the
 // tile size) but drops the fp32 dQ accumulator, its zeroing, its conversion
 // pass and all atomic traffic.
 //
-// LDS tiles read both row-wise and by transpose reads use the chunk swizzle of
-// cdna4.h; a tile read only row-wise is padded by 8 halves per row.
+// Tiles reach LDS through direct global-to-LDS copies issued two tiles ahead
+// (cdna4.h dma16/dma4), one barrier per tile. Every tile uses the chunk
+// swizzle of cdna4.h, so row reads and transpose reads are free of bank
+// conflicts; all LDS operand addresses are per-lane offsets fixed for the
+// whole loop.
 #include "cdna4.h"
 #include "kernels.h"
 
 namespace cgqa {
 namespace {
 
-constexpr int kBC = 64;               // keys per tile (dq kernel)
-constexpr int kWavesK = 4;            // waves per dkdv work-group, 32 keys each
-constexpr int kBK = 32 * kWavesK;     // keys per dkdv work-group
+constexpr int kBC = 64;         // keys per K/V tile (dq kernel)
+constexpr int kDqStages = 3;    // K/V ring depth (dq kernel)
+constexpr int kKvStages = 4;    // Q/dO ring depth (dkdv kernel)
+constexpr int kBK = 128;        // keys per dkdv work-group (4 x 32)
+constexpr int kBwdThreads = 512;
 
 struct BwdParams {
   const f16* __restrict__ q;
@@ -50,6 +59,7 @@ struct BwdParams {
   const f16* __restrict__ dout;
   const int32_t* __restrict__ cu;
   float* __restrict__ drow;  // workspace: fp32 [h_q, T], rowsum(dO * O)
+  float* __restrict__ lse2;  // workspace: fp32 [h_q, T], LSE * log2(e)
   f16* __restrict__ dq;
   f16* __restrict__ dk;
   f16* __restrict__ dv;
@@ -57,15 +67,21 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
-template <int D, int NTH>
-__global__ __launch_bounds__(NTH, 2) void dq_kernel(BwdParams p) {
-  constexpr int NT = D / 16;  // MFMA k-steps over the head dimension
-  constexpr int ND = D / 32;  // 32-wide output blocks over the head dimension
-  constexpr int CH = D / 8;   // 16-byte chunks per row
-  constexpr int VP = D + 8;   // V tile pitch (row reads only)
-  constexpr int CPT = (kBC * CH + NTH - 1) / NTH;
-  __shared__ __attribute__((aligned(16))) f16 Ks[2][kBC * D];  // swizzled
-  __shared__ __attribute__((aligned(16))) f16 Vs[2][kBC * VP];
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
+  constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CH; // tile rows per copy instruction
+  constexpr int CPW = kBC * CH / 64 / 8;  // copy instructions per wave per tensor
+  static_assert(CPW >= 1 && kBC * CH == 64 * 8 * CPW, "tile must split over the waves");
+  constexpr int TILE = kBC * D;
+  // K and V rings (chunk swizzle, unpadded so the copies fill them in lane
+  // order); after the loop the same memory holds the dQ^T partials.
+  __shared__ __attribute__((aligned(16))) f16 smem[2 * kDqStages * TILE];
+  static_assert(4 * ND * 16 * 64 * 4 <= (int)sizeof(smem), "reduction must fit the ring");
+  f16* const Ks = smem;
+  f16* const Vs = smem + kDqStages * TILE;
 
   const int BR = 32 * p.nqb;
   const int per = p.n_seqs * p.h_kv * p.n_chunks;
@@ -82,15 +98,17 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(BwdParams p) {
   const int n_kt = (min(L, q_wg0 + BR) + kBC - 1) / kBC;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int grp = lane >> 4;
   const int j16 = lane & 15;
-  const int hig = chunk * p.hpw + wave / p.nqb;
+  const int slot = wave & 3;  // (head, query block) slot
+  const int kh = wave >> 2;   // key half of every tile
+  const int hig = chunk * p.hpw + slot / p.nqb;
   const int head = g * p.G + min(hig, p.G - 1);
-  const int q0 = q_wg0 + (wave % p.nqb) * 32;
+  const int q0 = q_wg0 + (slot % p.nqb) * 32;
   const int qpos = q0 + l32;
   const bool wave_has_rows = q0 < L && hig < p.G;
   const bool qvalid = qpos < L && hig < p.G;
@@ -112,118 +130,160 @@ __global__ __launch_bounds__(NTH, 2) void dq_kernel(BwdParams p) {
   }
   dsum = half_swap_sum(dsum);  // D = rowsum(dO * O) over both halves of the row
   const float lse2 = p.lse[(size_t)head * p.T + qrow] * kLog2e;
-  if (qvalid && hi == 0) p.drow[(size_t)head * p.T + s0 + qpos] = dsum;
-
-  f16x8 kst[CPT], vst[CPT];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = min(tid + i * NTH, kBC * CH - 1);
-      const int r = c / CH;
-      const int key = min(kt * kBC + r, L - 1);
-      const size_t off = ((size_t)(s0 + key) * p.h_kv + g) * D + (c - r * CH) * 8;
-      kst[i] = *(const f16x8*)(p.k + off);
-      vst[i] = *(const f16x8*)(p.v + off);
-    }
-  };
-  // Keys past the end become zero rows (their scores are masked and their
-  // dS is zero, so only finiteness matters).
-  auto store_tile = [&](int kt, int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NTH;
-      if (c < kBC * CH) {
-        const int r = c / CH;
-        const int cc = c - r * CH;
-        const bool ok = kt * kBC + r < L;
-        *(f16x8*)(Ks[buf] + r * D + swz<D>(r, cc * 8)) = ok ? kst[i] : zero_f16x8();
-        *(f16x8*)(Vs[buf] + r * VP + cc * 8) = ok ? vst[i] : zero_f16x8();
-      }
-    }
-  };
-
-  f32x16 dq_acc[ND];  // dQ^T: rows = head dim, cols = queries
-#pragma unroll
-  for (int db = 0; db < ND; ++db) dq_acc[db] = zero_f32x16();
-
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);
-
-    if (wave_has_rows && kt * kBC <= q0 + 31) {
-      const f16* Kb = Ks[buf];
-      const f16* Vb = Vs[buf];
-      const bool diag = kt * kBC + kBC - 1 > q0;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T for 32 keys (accumulator element i:
-        // key kt*64 + 32kb + 8(i/4) + 4hi + i%4, query qpos).
-        f32x16 s = zero_f32x16(), dp = zero_f32x16();
-        const int kr = kb * 32 + l32;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          s = mfma32x32x16(*(const f16x8*)(Kb + kr * D + swz<D>(kr, 16 * t + 8 * hi)), qf[t], s);
-          dp = mfma32x32x16(*(const f16x8*)(Vb + kr * VP + 16 * t + 8 * hi), dof[t], dp);
-        }
-        f16x8 dsf[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(fmaf(s[i], p.scale_log2, -lse2));
-          if (diag) {
-            const int key = kt * kBC + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key > qpos) pv = 0.f;
-          }
-          dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
-        }
-        // dQ^T += K^T dS^T over these 32 keys; K^T by transpose reads of the
-        // K tile (A slot e of half hi <-> key 16u + 8(e/4) + 4hi + e%4).
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r0 = kb * 32 + 16 * u + 4 * hi + (j16 >> 2);
-            const int r1 = r0 + 8;
-            const f16x8 a = cat4(lds_read_tr(Kb + r0 * D + swz<D>(r0, col)),
-                                 lds_read_tr(Kb + r1 * D + swz<D>(r1, col)));
-            dq_acc[db] = mfma32x32x16(a, dsf[u], dq_acc[db]);
-          }
-        }
-      }
-    }
-
-    if (more) store_tile(kt + 1, buf ^ 1);
-    __syncthreads();
+  if (kh == 0 && qvalid && hi == 0) {
+    p.drow[(size_t)head * p.T + s0 + qpos] = dsum;
+    p.lse2[(size_t)head * p.T + s0 + qpos] = lse2;
   }
 
-  if (!qvalid) return;
+  // Copy of K/V tile kt into ring stage st: instruction i fills tile rows
+  // i * RPI + lane / CH; lane l lands in chunk slot l % CH of its row and
+  // fetches the global chunk the swizzle maps there. Keys past the sequence
+  // fetch its last row (their scores are masked).
+  auto issue_tile = [&](int kt, int st) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int i = wave * CPW + c;
+      const int r = i * RPI + lane / CH;
+      const int sl = (lane % CH) * 8;
+      const size_t row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
+      dma16(p.k + row + swz<D>(r, sl), Ks + st * TILE + i * 512);
+      dma16(p.v + row + swz<D>(r, sl), Vs + st * TILE + i * 512);
+    }
+  };
+
+  // Per-lane LDS offsets (halves), fixed for the loop; the swizzle depends on
+  // the row only through row % 16.
+  int koff[NT];  // K / V row 32kh + l32, columns 16t + 8hi
+#pragma unroll
+  for (int t = 0; t < NT; ++t) koff[t] = (32 * kh + l32) * D + swz<D>(l32, 16 * t + 8 * hi);
+  // K^T transpose reads: rows 32kh + 16u + 4hi + j16/4 (and 8 further),
+  // columns 32db + 16(grp&1) + 4(j16&3); A slot e of half hi <-> key
+  // 16u + 8(e/4) + 4hi + e%4 of the wave's half, as in the dS^T B operand.
+  int ktr0[ND], ktr1[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
+    const int r0 = 4 * hi + (j16 >> 2);
+    const int r1 = r0 + 8;
+    ktr0[db] = (32 * kh + r0) * D + swz<D>(r0, col);
+    ktr1[db] = (32 * kh + r1) * D + swz<D>(r1, col);
+  }
+
+  f32x16 acc[ND];  // dQ^T partial over this key half: rows = head dim, cols = queries
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
+
+  // The ordinary loads above are waited for here, before the first copy, so
+  // the compiler places no wait of its own inside the loop.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  issue_tile(0, 0);
+  if (n_kt > 1) issue_tile(1, 1);
+  int st = 0;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // Tile kt has landed for every wave, and every wave is done with kt - 1.
+    if (kt + 1 < n_kt) wait_vm_barrier<2 * CPW>();
+    else wait_vm_barrier<0>();
+    if (kt + 2 < n_kt) issue_tile(kt + 2, st == 0 ? 2 : st - 1);
+    const int k0 = kt * kBC + 32 * kh;  // first key of this wave's half
+    if (wave_has_rows && k0 <= q0 + 31) {
+      const f16* Kb = Ks + st * TILE;
+      const f16* Vb = Vs + st * TILE;
+      // Operand reads are issued in blocks ahead of their uses (scheduling
+      // fences keep the compiler from sinking them): the K/V row fragments,
+      // then, behind the S^T / dP^T matrix work, the K^T fragments.
+      f16x8 kfr[NT], vfr[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        kfr[t] = *(const f16x8*)(Kb + koff[t]);
+        vfr[t] = *(const f16x8*)(Vb + koff[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // S^T and dP^T for 32 keys (accumulator element i: key
+      // k0 + 8(i/4) + 4hi + i%4, query qpos).
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s = mfma32x32x16(kfr[t], qf[t], s);
+        dp = mfma32x32x16(vfr[t], dof[t], dp);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 kt_fr[ND][2];
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          kt_fr[db][u] = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
+                              lds_read_tr(Kb + ktr1[db] + 16 * u * D));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bool diag = k0 + 31 > q0;
+      f16x8 dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(s[i], p.scale_log2, -lse2));
+        if (diag && k0 + 8 * (i >> 2) + 4 * hi + (i & 3) > qpos) pv = 0.f;
+        dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dQ^T += K^T dS^T over the 32 keys.
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) acc[db] = mfma32x32x16(kt_fr[db][u], dsf[u], acc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st = st == 2 ? 0 : st + 1;
+  }
+
+  // Add the two key halves: waves 4..7 park their partials in the (now idle)
+  // ring, lane-contiguous 16-byte groups, and waves 0..3 add them.
+  __syncthreads();
+  float* red = (float*)smem + slot * (ND * 16 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * r4 + e];
+        *(f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4) = w;
+      }
+    }
+  }
+  __syncthreads();
+  if (kh == 1 || !qvalid) return;
   f16* dqrow = p.dq + ((size_t)(s0 + qpos) * p.h_q + head) * D;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 o2 = *(const f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4);
       f16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (f16)(dq_acc[db][4 * r4 + e] * p.scale);
+      for (int e = 0; e < 4; ++e) w[e] = (f16)((acc[db][4 * r4 + e] + o2[e]) * p.scale);
       *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = w;
     }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NT = D / 16;
   constexpr int ND = D / 32;
   constexpr int CH = D / 8;
-  constexpr int CPT = (32 * CH + 255) / 256;  // chunks per thread of a Q (or dO) block
-  __shared__ __attribute__((aligned(16))) f16 Qs[2][32 * D];   // swizzled
-  __shared__ __attribute__((aligned(16))) f16 dOs[2][32 * D];  // swizzled
-  __shared__ __attribute__((aligned(16))) float lse_s[2][32];
-  __shared__ __attribute__((aligned(16))) float drow_s[2][32];
+  constexpr int RPI = 64 / CH;
+  constexpr int IPB = 32 * CH / 64;  // copy instructions per 32-row block of one tensor
+  constexpr int CPW = 2 * IPB / 8;   // copy instructions per wave per block (Q and dO)
+  static_assert(CPW >= 1 && 2 * IPB == 8 * CPW, "block must split over the waves");
+  constexpr int BLK = 32 * D;
+  // Ring of query blocks: [stage][Q, dO] tiles (chunk swizzle) and, per
+  // stage, LSE * log2(e) (32 floats) then D (32 floats) of the block's rows.
+  __shared__ __attribute__((aligned(16))) f16 Xs[kKvStages][2][BLK];
+  __shared__ __attribute__((aligned(16))) float Ls[kKvStages][64];
+  // P hand-off, [block parity][wave pair][two 16-byte groups per lane].
+  __shared__ __attribute__((aligned(16))) f16 Px[2][4][2 * 64 * 8];
 
   // Key tile 0 of every (sequence, KV head) sees the most query rows: first.
   const int per = p.n_seqs * p.h_kv;
@@ -237,26 +297,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   if (k_wg0 >= L) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int grp = lane >> 4;
   const int j16 = lane & 15;
-  const int kw0 = k_wg0 + 32 * wave;  // first key of this wave
+  // Waves w and w + 4 share a SIMD (measured on gfx950): one of each team,
+  // so one's matrix work overlaps the other's arithmetic.
+  const int team = wave >> 2;  // 0: S, P, dV;  1: dP, dS, dK (one block behind)
+  const int w4 = wave & 3;
+  const int kw0 = k_wg0 + 32 * w4;  // first key of this wave pair
   const int key = kw0 + l32;
-  const bool kvalid = key < L;
 
-  // K^T and V^T B operands of this wave: lane holds row `key` (rows past the
-  // end read the last row: their scores are masked), columns 16t + 8hi .. +7.
-  f16x8 kf[NT], vf[NT];
+  // K (team 0) or V (team 1) of the pair's keys as the B operand: lane holds
+  // row `key` (rows past the end read the last row; never stored), columns
+  // 16t + 8hi .. +7.
+  f16x8 kvf[NT];
   {
-    const size_t off = ((size_t)(s0 + min(key, L - 1)) * p.h_kv + g) * D + 8 * hi;
+    const f16* src = (team ? p.v : p.k) + ((size_t)(s0 + min(key, L - 1)) * p.h_kv + g) * D + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      kf[t] = *(const f16x8*)(p.k + off + 16 * t);
-      vf[t] = *(const f16x8*)(p.v + off + 16 * t);
-    }
+    for (int t = 0; t < NT; ++t) kvf[t] = *(const f16x8*)(src + 16 * t);
   }
 
   // Query blocks at or after the key tile, for each head of the group.
@@ -264,119 +325,157 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   const int n_qb = (L + 31) / 32 - qb_begin;
   const int n_it = p.G * n_qb;
 
-  f16x8 qst[CPT], dst[CPT];
-  float aux = 0.f;  // lse (threads 0..31) or D (threads 32..63) of the staged block
-  auto load_blk = [&](int it) {
-    const int head = g * p.G + it / n_qb;
-    const int q0 = (qb_begin + it % n_qb) * 32;
+  // Copy of block m into stage st. Instruction i (of 2 * IPB) fills rows
+  // (i % IPB) * RPI + lane / CH of Q (i < IPB) or dO; wave 0 also copies the
+  // row terms. Rows past the sequence fetch its last row; the mask below
+  // zeroes their weights.
+  auto issue_blk = [&](int m, int st) {
+    const int head = g * p.G + m / n_qb;
+    const int q0 = (qb_begin + m % n_qb) * 32;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = min(tid + i * 256, 32 * CH - 1);
-      const int r = c / CH;
-      const size_t off =
-          ((size_t)(s0 + min(q0 + r, L - 1)) * p.h_q + head) * D + (c - r * CH) * 8;
-      qst[i] = *(const f16x8*)(p.q + off);
-      dst[i] = *(const f16x8*)(p.dout + off);
+    for (int c = 0; c < CPW; ++c) {
+      const int i = wave * CPW + c;
+      const int tsel = i / IPB;
+      const int ii = i % IPB;
+      const int r = ii * RPI + lane / CH;
+      const int sl = (lane % CH) * 8;
+      const f16* src = (tsel ? p.dout : p.q) +
+                       ((size_t)(s0 + min(q0 + r, L - 1)) * p.h_q + head) * D + swz<D>(r, sl);
+      dma16(src, &Xs[st][tsel][ii * 512]);
     }
-    if (tid < 64) {
-      const size_t ix = (size_t)head * p.T + s0 + min(q0 + (tid & 31), L - 1);
-      aux = tid < 32 ? p.lse[ix] : p.drow[ix];
-    }
-  };
-  auto store_blk = [&](int it, int buf) {
-    const int q0 = (qb_begin + it % n_qb) * 32;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * 256;
-      if (c < 32 * CH) {
-        const int r = c / CH;
-        const int cc = c - r * CH;
-        *(f16x8*)(Qs[buf] + r * D + swz<D>(r, cc * 8)) = qst[i];
-        *(f16x8*)(dOs[buf] + r * D + swz<D>(r, cc * 8)) = dst[i];
-      }
-    }
-    if (tid < 64) {
-      const bool ok = q0 + (tid & 31) < L;  // rows past the end: P = 0
-      if (tid < 32) lse_s[buf][tid] = ok ? aux * kLog2e : INFINITY;
-      else drow_s[buf][tid - 32] = ok ? aux : 0.f;
+    if (wave == 0) {
+      const float* src = (lane < 32 ? p.lse2 : p.drow) + (size_t)head * p.T + s0 +
+                         min(q0 + l32, L - 1);
+      dma4(src, &Ls[st][0]);
     }
   };
 
-  f32x16 dk_acc[ND], dv_acc[ND];  // dK^T, dV^T: rows = head dim, cols = keys
+  // Per-lane LDS offsets (halves) within a block, fixed for the loop.
+  int xoff[NT];  // row l32, columns 16t + 8hi (first GEMM's A operand)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) xoff[t] = l32 * D + swz<D>(l32, 16 * t + 8 * hi);
+  // Transpose reads of rows 16u + 4hi + j16/4 (and 8 further), columns
+  // 32db + 16(grp&1) + 4(j16&3): A slot e of half hi <-> query row
+  // 16u + 8(e/4) + 4hi + e%4, the slot order of the P / dS B operand.
+  int yoff0[ND], yoff1[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
-    dk_acc[db] = zero_f32x16();
-    dv_acc[db] = zero_f32x16();
+    const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
+    const int r0 = 4 * hi + (j16 >> 2);
+    const int r1 = r0 + 8;
+    yoff0[db] = r0 * D + swz<D>(r0, col);
+    yoff1[db] = r1 * D + swz<D>(r1, col);
   }
 
-  load_blk(0);
-  store_blk(0, 0);
-  __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < n_it;
-    if (more) load_blk(it + 1);
-    const int q0 = (qb_begin + it % n_qb) * 32;
-
-    // Waves whose keys all lie after the block's last query see only masked pairs.
-    if (kw0 <= q0 + 31 && kw0 < L) {
-      const f16* Qb = Qs[buf];
-      const f16* dOb = dOs[buf];
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+  f32x16 acc[ND];  // dV^T (team 0) or dK^T (team 1): rows = head dim, cols = keys
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int col = swz<D>(l32, 16 * t + 8 * hi);
-        s = mfma32x32x16(*(const f16x8*)(Qb + l32 * D + col), kf[t], s);
-        dp = mfma32x32x16(*(const f16x8*)(dOb + l32 * D + col), vf[t], dp);
-      }
-      // Accumulator element i: query row q0 + 8(i/4) + 4hi + i%4, key `key`.
-      const bool need_mask = kw0 + 31 > q0;
-      f16x8 pf[2], dsf[2];
+  for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
+
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): see dq_kernel
+  issue_blk(0, 0);
+  if (n_it > 1) issue_blk(1, 1);
+  for (int j = 0; j <= n_it; ++j) {
+    // Block j has landed for every wave (block j + 1 may still be in
+    // flight), every wave is done with its block of the previous iteration,
+    // and team 0's P of block j - 1 is in LDS.
+    if (j + 1 < n_it) {
+      if (wave == 0) wait_vm_barrier<CPW + 1>();
+      else wait_vm_barrier<CPW>();
+    } else {
+      wait_vm_barrier<0>();
+    }
+    // Stage (j + 2) % 4 last held block j - 2, which team 1 finished in the
+    // previous iteration.
+    if (j + 2 < n_it) issue_blk(j + 2, (j + 2) % kKvStages);
+    const int m = j - team;
+    if (m < 0 || m >= n_it) continue;  // uniform over the wave
+    const int st = m % kKvStages;
+    const int q0 = (qb_begin + m % n_qb) * 32;
+    const f16* X = Xs[st][team];      // rows: Q (team 0) or dO (team 1)
+    const f16* Y = Xs[st][1 - team];  // transposed: dO (team 0) or Q (team 1)
+
+    // Operand reads are issued in blocks ahead of their uses (scheduling
+    // fences keep the compiler from sinking them): the row fragments of the
+    // first product, then, behind its matrix work, the transposed fragments
+    // of the second, the row terms and the P hand-off.
+    f16x8 xfr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xfr[t] = *(const f16x8*)(X + xoff[t]);
+    __builtin_amdgcn_sched_barrier(0);
+    // S = Q K^T (team 0) or dP = dO V^T (team 1); accumulator element i:
+    // query row q0 + 8(i/4) + 4hi + i%4, key `key`.
+    // Two interleaved chains over even / odd k-steps (a single dependent
+    // chain would leave the matrix core idle between products).
+    f32x16 sa = zero_f32x16(), sb = zero_f32x16();
+#pragma unroll
+    for (int t = 0; t < NT; t += 2) {
+      sa = mfma32x32x16(xfr[t], kvf[t], sa);
+      sb = mfma32x32x16(xfr[t + 1], kvf[t + 1], sb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sa += sb;
+    f16x8 yfr[ND][2];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        yfr[db][u] = cat4(lds_read_tr(Y + yoff0[db] + 16 * u * D),
+                          lds_read_tr(Y + yoff1[db] + 16 * u * D));
+    }
+    // Row terms of the same rows: 4 groups of 4 consecutive rows.
+    const float* lrow = &Ls[st][32 * team + 4 * hi];
+    f32x4 l4[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) l4[jj] = *(const f32x4*)(lrow + 8 * jj);
+    f16* px = &Px[m & 1][w4][lane * 8];
+    f16x8 p0, p1;
+    if (team == 1) {
+      p0 = *(const f16x8*)px;
+      p1 = *(const f16x8*)(px + 512);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 f[2];
+    if (team == 0) {
+      // Causal mask on diagonal blocks, row mask on the sequence's last block.
+      const bool need_mask = kw0 + 31 > q0 || q0 + 31 >= L;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int qr = 8 * (i >> 2) + 4 * hi + (i & 3);
-        float pv = fast_exp2(fmaf(s[i], p.scale_log2, -lse_s[buf][qr]));
-        if (need_mask && key > q0 + qr) pv = 0.f;
-        pf[i >> 3][i & 7] = (f16)pv;
-        dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - drow_s[buf][qr]));
+        const int qr = q0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        float pv = fast_exp2(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
+        if (need_mask && (key > qr || qr >= L)) pv = 0.f;
+        f[i >> 3][i & 7] = (f16)pv;
       }
-      // dV^T += dO^T P and dK^T += Q^T dS; A-operand slot e of half hi holds
-      // query row 16u + 8(e/4) + 4hi + e%4, matching the B slots.
+      *(f16x8*)px = f[0];
+      *(f16x8*)(px + 512) = f[1];
+    } else {
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r0 = 16 * u + 4 * hi + (j16 >> 2);
-          const int r1 = r0 + 8;
-          const int c0 = swz<D>(r0, col), c1 = swz<D>(r1, col);
-          const f16x8 a_do = cat4(lds_read_tr(dOb + r0 * D + c0), lds_read_tr(dOb + r1 * D + c1));
-          dv_acc[db] = mfma32x32x16(a_do, pf[u], dv_acc[db]);
-          const f16x8 a_q = cat4(lds_read_tr(Qb + r0 * D + c0), lds_read_tr(Qb + r1 * D + c1));
-          dk_acc[db] = mfma32x32x16(a_q, dsf[u], dk_acc[db]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+        f[i >> 3][i & 7] = (f16)(pv * (sa[i] - l4[i >> 2][i & 3]));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    if (more) store_blk(it + 1, buf ^ 1);
-    __syncthreads();
+    // dV^T += dO^T P (team 0) or dK^T += Q^T dS (team 1).
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db) acc[db] = mfma32x32x16(yfr[db][u], f[u], acc[db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (!kvalid) return;
-  const size_t off = ((size_t)(s0 + key) * p.h_kv + g) * D;
+  if (key >= L) return;
+  f16* dst = (team ? p.dk : p.dv) + ((size_t)(s0 + key) * p.h_kv + g) * D;
+  const float sc = team ? p.scale : 1.f;
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      f16x4 wk, wv;
+      f16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wk[e] = (f16)(dk_acc[db][4 * r4 + e] * p.scale);
-        wv[e] = (f16)dv_acc[db][4 * r4 + e];
-      }
-      const int d = 32 * db + 8 * r4 + 4 * hi;
-      *(f16x4*)(p.dk + off + d) = wk;
-      *(f16x4*)(p.dv + off + d) = wv;
+      for (int e = 0; e < 4; ++e) w[e] = (f16)(acc[db][4 * r4 + e] * sc);
+      *(f16x4*)(dst + 32 * db + 8 * r4 + 4 * hi) = w;
     }
   }
 }
@@ -393,6 +492,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.dout = (const f16*)a.dout;
   p.cu = a.cu_seqlens;
   p.drow = a.drow;
+  p.lse2 = a.lse2;
   p.dq = (f16*)a.dq;
   p.dk = (f16*)a.dk;
   p.dv = (f16*)a.dv;
@@ -401,7 +501,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
   p.G = a.h_q / a.h_kv;
-  p.hpw = p.G < 4 ? p.G : 4;
+  // dq work-groups: four (head, 32-row block) slots; hpw heads of the group
+  // (the largest power of two <= min(G, 4)) times 4 / hpw query blocks.
+  p.hpw = 1;
+  while (p.hpw * 2 <= p.G && p.hpw * 2 <= 4) p.hpw *= 2;
   p.nqb = 4 / p.hpw;
   p.n_chunks = (p.G + p.hpw - 1) / p.hpw;
   p.n_qtiles = (a.max_seqlen + 32 * p.nqb - 1) / (32 * p.nqb);
@@ -410,15 +513,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.scale_log2 = a.scale * kLog2e;
   const dim3 gq(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
-  const int nth = 64 * p.hpw * p.nqb;  // 256, or 192 when G == 3
   if (a.head_dim == 128) {
-    if (nth == 256) hipLaunchKernelGGL((dq_kernel<128, 256>), gq, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((dq_kernel<128, 192>), gq, dim3(192), 0, stream, p);
-    hipLaunchKernelGGL(dkdv_kernel<128>, gk, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dq_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL(dkdv_kernel<128>, gk, dim3(kBwdThreads), 0, stream, p);
   } else {
-    if (nth == 256) hipLaunchKernelGGL((dq_kernel<64, 256>), gq, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((dq_kernel<64, 192>), gq, dim3(192), 0, stream, p);
-    hipLaunchKernelGGL(dkdv_kernel<64>, gk, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dq_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL(dkdv_kernel<64>, gk, dim3(kBwdThreads), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -73,8 +73,12 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   const int BR = 32 * p.nqb;
   // Heaviest query tiles (the last ones of the longest sequences) first.
   const int per = p.n_seqs * p.h_kv * p.n_chunks;
-  const int qt = p.n_qtiles - 1 - (int)blockIdx.x / per;
-  int rem = (int)blockIdx.x % per;
+  // Work-group and lane ids come straight from the hardware registers: this
+  // file is built without IEEE mode, so device-library helpers (compiled
+  // with it) are not inlined here and none may be called.
+  const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+  const int qt = p.n_qtiles - 1 - wg / per;
+  int rem = wg % per;
   const int chunk = rem % p.n_chunks;
   rem /= p.n_chunks;
   const int g = rem % p.h_kv;
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   if (q_wg0 >= L) return;  // uniform over the work-group
   const int n_kt = (min(L, q_wg0 + BR) + kBC - 1) / kBC;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
       *(f16x4*)(orow + 32 * db + 8 * r4 + 4 * hi) = w;
     }
   }
-  if (hi == 0) p.lse[(size_t)head * p.T + s0 + qpos] = m_run * kLn2 + logf(l_tot);
+  if (hi == 0) p.lse[(size_t)head * p.T + s0 + qpos] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace

@@ -62,6 +62,15 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane index (0..63) recomputed where it is used (two VALU instructions that
+// the compiler can neither hoist nor keep live), for per-lane constants that
+// are cheaper to rebuild than to hold in registers through a loop.
+__device__ __forceinline__ int lane_id_fresh() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
 __device__ __forceinline__ f16x8 zero_f16x8() { return f16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
 
 // Column (in halves) of element (row, col) in an LDS tile of D-half rows with
@@ -105,6 +114,25 @@ __device__ __forceinline__ void dma16(const void* gptr, f16* lds_wave_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Same copy with a wave-uniform 64-bit base (kept in SGPRs) and a 32-bit
+// per-lane byte offset: one VGPR per lane instead of a 64-bit address.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, f16* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// 4-byte-per-lane variant (global_load_lds_dword): lane l's dword lands at
+// lds_wave_base + 4 l. Same rules as dma16.
+__device__ __forceinline__ void dma4(const void* gptr, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gptr)
                : "memory", "m0");
 }
 

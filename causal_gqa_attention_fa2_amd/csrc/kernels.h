@@ -31,6 +31,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* drow;    // workspace: fp32 [h_q, T], rowsum(dO * O)
+  float* lse2;    // workspace: fp32 [h_q, T], LSE * log2(e)
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   float scale;
 };

@@ -106,7 +106,8 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
                      float* lse, void* stream);
 
 /* Bytes of device workspace attn_bwd needs for `dims` (0 for an empty
- * batch). Holds the fp32 row terms D = rowsum(dO * O) [h_q, T]. */
+ * batch). Holds two fp32 [h_q, T] arrays of per-row terms: D = rowsum(dO * O)
+ * and LSE * log2(e). */
 size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims);
 
 /*
