@@ -7,7 +7,24 @@
 
 #include "kernels.h"
 
+#include <atomic>
+
 namespace {
+
+// Compute units of the current device (queried once per device; persistent
+// kernels launch at most one work-group per unit).
+int num_compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 constexpr size_t kWsAlign = 256;
 
@@ -151,6 +168,7 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.h_kv = dims->h_kv;
   a.head_dim = dims->head_dim;
   a.scale = scale;
+  a.num_cus = num_compute_units();
   return cgqa::launch_bwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -76,26 +76,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   constexpr int CPW = kBC * CH / 64 / 8;  // copy instructions per wave per tensor
   static_assert(CPW >= 1 && kBC * CH == 64 * 8 * CPW, "tile must split over the waves");
   constexpr int TILE = kBC * D;
-  // K and V rings (chunk swizzle, unpadded so the copies fill them in lane
-  // order); after the loop the same memory holds the dQ^T partials.
+  // Ring stage st holds the K tile at smem + 2 st TILE and the V tile right
+  // after it (chunk swizzle, unpadded so the copies fill them in lane order).
+  // At the end of each work item the dQ^T partials are added through stages
+  // 0 and 1 while stage 2 already receives the next item's first tile.
   __shared__ __attribute__((aligned(16))) f16 smem[2 * kDqStages * TILE];
-  static_assert(4 * ND * 16 * 64 * 4 <= (int)sizeof(smem), "reduction must fit the ring");
-  f16* const Ks = smem;
-  f16* const Vs = smem + kDqStages * TILE;
-
-  const int BR = 32 * p.nqb;
-  const int per = p.n_seqs * p.h_kv * p.n_chunks;
-  const int qt = p.n_qtiles - 1 - (int)blockIdx.x / per;  // heaviest tiles first
-  int rem = (int)blockIdx.x % per;
-  const int chunk = rem % p.n_chunks;
-  rem /= p.n_chunks;
-  const int g = rem % p.h_kv;
-  const int b = rem / p.h_kv;
-  const int s0 = p.cu[b];
-  const int L = p.cu[b + 1] - s0;
-  const int q_wg0 = qt * BR;
-  if (q_wg0 >= L) return;  // uniform over the work-group
-  const int n_kt = (min(L, q_wg0 + BR) + kBC - 1) / kBC;
+  static_assert(kDqStages == 3, "the item hand-over below assumes three stages");
+  static_assert(4 * ND * 16 * 64 * 4 <= 2 * 2 * TILE * 2, "reduction must fit stages 0 and 1");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -106,53 +93,103 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   const int j16 = lane & 15;
   const int slot = wave & 3;  // (head, query block) slot
   const int kh = wave >> 2;   // key half of every tile
-  const int hig = chunk * p.hpw + slot / p.nqb;
-  const int head = g * p.G + min(hig, p.G - 1);
-  const int q0 = q_wg0 + (slot % p.nqb) * 32;
-  const int qpos = q0 + l32;
-  const bool wave_has_rows = q0 < L && hig < p.G;
-  const bool qvalid = qpos < L && hig < p.G;
-  const int qrow = s0 + min(qpos, L - 1);  // rows past the end read the last row
 
-  // Q^T and dO^T as B operands: lane holds row qpos, columns 16t + 8hi .. +7.
-  f16x8 qf[NT], dof[NT];
-  float dsum = 0.f;
-  {
-    const size_t off = ((size_t)qrow * p.h_q + head) * D + 8 * hi;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      qf[t] = *(const f16x8*)(p.q + off + 16 * t);
-      dof[t] = *(const f16x8*)(p.dout + off + 16 * t);
-      const f16x8 ot = *(const f16x8*)(p.o + off + 16 * t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsum += (float)dof[t][e] * (float)ot[e];
+  // Persistent work-groups: item i is query tile n_qtiles - 1 - i / per of
+  // (sequence, KV head, head chunk) i % per, so items run heaviest first.
+  // Work-groups are dealt to the 8 XCDs round-robin (w % 8), each with its
+  // own L2: work-group w takes only items i = x + 8 j with x = w % 8, so the
+  // query tiles of one (sequence, KV head) share an L2 as they did with one
+  // work-group per item. Within class x the nwx groups of that XCD take
+  // j = r nwx + wx (r even) or r nwx + nwx - 1 - wx (r odd) in rounds r
+  // (snake order keeps the per-group sums even). Staying resident lets a
+  // group overlap the start of its next item (first K/V copies, row loads)
+  // with the end of the current one.
+  constexpr int kXcds = 8;
+  const int BR = 32 * p.nqb;
+  const int per = p.n_seqs * p.h_kv * p.n_chunks;
+  const int n_items = p.n_qtiles * per;
+  const int NW = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
+  const int xcd = w % kXcds;
+  const int wx = w / kXcds;
+  const int nwx = (NW - xcd + kXcds - 1) / kXcds;  // groups on this XCD
+  auto item_of = [&](int r) {
+    const int j = r * nwx + ((r & 1) ? nwx - 1 - wx : wx);
+    return xcd + kXcds * j;
+  };
+  struct Item {
+    int b, g, chunk, s0, L, q_wg0, n_kt;
+  };
+  auto decode = [&](int i) {
+    Item it;
+    const int qt = p.n_qtiles - 1 - i / per;
+    int rem = i % per;
+    it.chunk = rem % p.n_chunks;
+    rem /= p.n_chunks;
+    it.g = rem % p.h_kv;
+    it.b = rem / p.h_kv;
+    it.s0 = p.cu[it.b];
+    it.L = p.cu[it.b + 1] - it.s0;
+    it.q_wg0 = qt * BR;
+    it.n_kt = it.q_wg0 < it.L ? (min(it.L, it.q_wg0 + BR) + kBC - 1) / kBC : 0;
+    return it;
+  };
+  // Next non-empty item from round r on (n_items if none).
+  auto next_item = [&](int& r) {
+    for (;; ++r) {
+      const int i = item_of(r);
+      if (i >= n_items) return n_items;
+      if (decode(i).n_kt > 0) return i;
     }
-  }
-  dsum = half_swap_sum(dsum);  // D = rowsum(dO * O) over both halves of the row
-  const float lse2 = p.lse[(size_t)head * p.T + qrow] * kLog2e;
-  if (kh == 0 && qvalid && hi == 0) {
-    p.drow[(size_t)head * p.T + s0 + qpos] = dsum;
-    p.lse2[(size_t)head * p.T + s0 + qpos] = lse2;
-  }
+  };
 
-  // Copy of K/V tile kt into ring stage st: instruction i fills tile rows
-  // i * RPI + lane / CH; lane l lands in chunk slot l % CH of its row and
-  // fetches the global chunk the swizzle maps there. Keys past the sequence
-  // fetch its last row (their scores are masked).
-  auto issue_tile = [&](int kt, int st) {
+  // Copy of K/V tile kt of item `it` into ring stage st: instruction i fills
+  // tile rows i * RPI + lane / CH; lane l lands in chunk slot l % CH of its
+  // row and fetches the global chunk the swizzle maps there. Keys past the
+  // sequence fetch its last row (their scores are masked).
+  auto issue_tile = [&](const Item& it, int kt, int st) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int i = wave * CPW + c;
       const int r = i * RPI + lane / CH;
       const int sl = (lane % CH) * 8;
-      const size_t row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
-      dma16(p.k + row + swz<D>(r, sl), Ks + st * TILE + i * 512);
-      dma16(p.v + row + swz<D>(r, sl), Vs + st * TILE + i * 512);
+      const size_t row = ((size_t)(it.s0 + min(kt * kBC + r, it.L - 1)) * p.h_kv + it.g) * D;
+      f16* kst = smem + st * 2 * TILE;
+      dma16(p.k + row + swz<D>(r, sl), kst + i * 512);
+      dma16(p.v + row + swz<D>(r, sl), kst + TILE + i * 512);
+    }
+  };
+  // This wave's rows of item `it`.
+  struct Rows {
+    int head, q0, qpos, qrow;
+    bool has_rows, valid;
+  };
+  auto rows_of = [&](const Item& it) {
+    Rows rw;
+    const int hig = it.chunk * p.hpw + slot / p.nqb;
+    rw.head = it.g * p.G + min(hig, p.G - 1);
+    rw.q0 = it.q_wg0 + (slot % p.nqb) * 32;
+    rw.qpos = rw.q0 + l32;
+    rw.has_rows = rw.q0 < it.L && hig < p.G;
+    rw.valid = rw.qpos < it.L && hig < p.G;
+    rw.qrow = it.s0 + min(rw.qpos, it.L - 1);  // rows past the end read the last row
+    return rw;
+  };
+  // Q^T and dO^T as B operands (lane holds row qpos, columns 16t + 8hi .. +7)
+  // and O for the row terms.
+  f16x8 qf[NT], dof[NT], of[NT];
+  auto load_rows = [&](const Rows& rw) {
+    const size_t off = ((size_t)rw.qrow * p.h_q + rw.head) * D + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      qf[t] = *(const f16x8*)(p.q + off + 16 * t);
+      dof[t] = *(const f16x8*)(p.dout + off + 16 * t);
+      of[t] = *(const f16x8*)(p.o + off + 16 * t);
     }
   };
 
-  // Per-lane LDS offsets (halves), fixed for the loop; the swizzle depends on
-  // the row only through row % 16.
+  // Per-lane LDS offsets (halves), fixed for the kernel; the swizzle depends
+  // on the row only through row % 16.
   int koff[NT];  // K / V row 32kh + l32, columns 16t + 8hi
 #pragma unroll
   for (int t = 0; t < NT; ++t) koff[t] = (32 * kh + l32) * D + swz<D>(l32, 16 * t + 8 * hi);
@@ -169,102 +206,130 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     ktr1[db] = (32 * kh + r1) * D + swz<D>(r1, col);
   }
 
-  f32x16 acc[ND];  // dQ^T partial over this key half: rows = head dim, cols = queries
-#pragma unroll
-  for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
+  int round = 0;
+  int cur = next_item(round);
+  if (cur >= n_items) return;  // uniform over the work-group
+  Item it = decode(cur);
+  Rows rw = rows_of(it);
+  // The first tile's copies go out before the row loads, so the two
+  // latencies overlap instead of adding up.
+  issue_tile(it, 0, 0);
+  load_rows(rw);
+  int st0 = 0;  // ring stage of tile 0 of the current item
 
-  // The ordinary loads above are waited for here, before the first copy, so
-  // the compiler places no wait of its own inside the loop.
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  issue_tile(0, 0);
-  if (n_kt > 1) issue_tile(1, 1);
-  int st = 0;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    // Tile kt has landed for every wave, and every wave is done with kt - 1.
-    if (kt + 1 < n_kt) wait_vm_barrier<2 * CPW>();
-    else wait_vm_barrier<0>();
-    if (kt + 2 < n_kt) issue_tile(kt + 2, st == 0 ? 2 : st - 1);
-    const int k0 = kt * kBC + 32 * kh;  // first key of this wave's half
-    if (wave_has_rows && k0 <= q0 + 31) {
-      const f16* Kb = Ks + st * TILE;
-      const f16* Vb = Vs + st * TILE;
-      // Operand reads are issued in blocks ahead of their uses (scheduling
-      // fences keep the compiler from sinking them): the K/V row fragments,
-      // then, behind the S^T / dP^T matrix work, the K^T fragments.
-      f16x8 kfr[NT], vfr[NT];
+  for (;;) {
+    float dsum = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        kfr[t] = *(const f16x8*)(Kb + koff[t]);
-        vfr[t] = *(const f16x8*)(Vb + koff[t]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // S^T and dP^T for 32 keys (accumulator element i: key
-      // k0 + 8(i/4) + 4hi + i%4, query qpos).
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s = mfma32x32x16(kfr[t], qf[t], s);
-        dp = mfma32x32x16(vfr[t], dof[t], dp);
+      for (int e = 0; e < 8; ++e) dsum += (float)dof[t][e] * (float)of[t][e];
+    }
+    dsum = half_swap_sum(dsum);  // D = rowsum(dO * O) over both halves of the row
+    const float lse2 = p.lse[(size_t)rw.head * p.T + rw.qrow] * kLog2e;
+
+    f32x16 acc[ND];  // dQ^T partial over this key half: rows = head dim, cols = queries
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
+
+    // Everything in flight (tile 0's copies, the row loads, the previous
+    // item's stores) is waited for here, so the compiler places no wait of
+    // its own inside the loop; tile 1's copies go out after the wait.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    const int n_kt = it.n_kt;
+    int st = st0;
+    if (n_kt > 1) issue_tile(it, 1, st == 2 ? 0 : st + 1);
+    for (int kt = 0; kt < n_kt; ++kt) {
+      // Tile kt has landed for every wave, and every wave is done with kt - 1.
+      if (kt + 1 < n_kt) wait_vm_barrier<2 * CPW>();
+      else wait_vm_barrier<0>();
+      if (kt + 2 < n_kt) issue_tile(it, kt + 2, st == 0 ? 2 : st - 1);
+      const int k0 = kt * kBC + 32 * kh;  // first key of this wave's half
+      if (rw.has_rows && k0 <= rw.q0 + 31) {
+        const f16* Kb = smem + st * 2 * TILE;
+        const f16* Vb = Kb + TILE;
+        // S^T and dP^T for 32 keys (accumulator element i: key
+        // k0 + 8(i/4) + 4hi + i%4, query qpos), two interleaved chains.
+        f32x16 sv = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          sv = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], sv);
+          dp = mfma32x32x16(*(const f16x8*)(Vb + koff[t]), dof[t], dp);
+        }
+        const bool diag = k0 + 31 > rw.q0;
+        f16x8 dsf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
+          if (diag && k0 + 8 * (i >> 2) + 4 * hi + (i & 3) > rw.qpos) pv = 0.f;
+          dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
+        }
+        // dQ^T += K^T dS^T over the 32 keys (K^T by transpose reads).
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const f16x8 kt = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
+                                  lds_read_tr(Kb + ktr1[db] + 16 * u * D));
+            acc[db] = mfma32x32x16(kt, dsf[u], acc[db]);
+          }
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f16x8 kt_fr[ND][2];
+      st = st == 2 ? 0 : st + 1;
+    }
+
+    // Every wave is done with the ring. The next item's first tile goes to
+    // stage 2 and its row loads go out now (Q, dO and O of this item are no
+    // longer needed), so their latency hides behind this item's reduction.
+    __syncthreads();
+    ++round;
+    const int nxt = next_item(round);
+    const Item it_n = nxt < n_items ? decode(nxt) : it;
+    const Rows rw_n = rows_of(it_n);
+    const bool more = nxt < n_items;
+    if (more) {
+      issue_tile(it_n, 0, 2);
+      load_rows(rw_n);
+    }
+    // Row terms for the dK/dV kernel (nothing in this kernel waits for them).
+    if (kh == 0 && rw.valid && hi == 0) {
+      p.drow[(size_t)rw.head * p.T + rw.qrow] = dsum;
+      p.lse2[(size_t)rw.head * p.T + rw.qrow] = lse2;
+    }
+    // Add the two key halves: waves 4..7 park their partials in stages 0 and
+    // 1 (lane-contiguous 16-byte groups) and waves 0..3 add them.
+    float* red = (float*)smem + slot * (ND * 16 * 64);
+    if (kh == 1) {
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          kt_fr[db][u] = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
-                              lds_read_tr(Kb + ktr1[db] + 16 * u * D));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const bool diag = k0 + 31 > q0;
-      f16x8 dsf[2];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 wv;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(s[i], p.scale_log2, -lse2));
-        if (diag && k0 + 8 * (i >> 2) + 4 * hi + (i & 3) > qpos) pv = 0.f;
-        dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // dQ^T += K^T dS^T over the 32 keys.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int db = 0; db < ND; ++db) acc[db] = mfma32x32x16(kt_fr[db][u], dsf[u], acc[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    st = st == 2 ? 0 : st + 1;
-  }
-
-  // Add the two key halves: waves 4..7 park their partials in the (now idle)
-  // ring, lane-contiguous 16-byte groups, and waves 0..3 add them.
-  __syncthreads();
-  float* red = (float*)smem + slot * (ND * 16 * 64);
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * r4 + e];
-        *(f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4) = w;
+          for (int e = 0; e < 4; ++e) wv[e] = acc[db][4 * r4 + e];
+          *(f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4) = wv;
+        }
       }
     }
-  }
-  __syncthreads();
-  if (kh == 1 || !qvalid) return;
-  f16* dqrow = p.dq + ((size_t)(s0 + qpos) * p.h_q + head) * D;
+    __syncthreads();
+    if (kh == 0 && rw.valid) {
+      f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
+      for (int db = 0; db < ND; ++db) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 o2 = *(const f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4);
-      f16x4 w;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 o2 = *(const f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4);
+          f16x4 wv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (f16)((acc[db][4 * r4 + e] + o2[e]) * p.scale);
-      *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = w;
+          for (int e = 0; e < 4; ++e) wv[e] = (f16)((acc[db][4 * r4 + e] + o2[e]) * p.scale);
+          *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = wv;
+        }
+      }
     }
+    if (!more) break;
+    __syncthreads();  // stages 0 and 1 are free again before tile 1's copies
+    it = it_n;
+    rw = rw_n;
+    st0 = 2;
   }
 }
 
@@ -310,16 +375,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   const int kw0 = k_wg0 + 32 * w4;  // first key of this wave pair
   const int key = kw0 + l32;
 
-  // K (team 0) or V (team 1) of the pair's keys as the B operand: lane holds
-  // row `key` (rows past the end read the last row; never stored), columns
-  // 16t + 8hi .. +7.
-  f16x8 kvf[NT];
-  {
-    const f16* src = (team ? p.v : p.k) + ((size_t)(s0 + min(key, L - 1)) * p.h_kv + g) * D + 8 * hi;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) kvf[t] = *(const f16x8*)(src + 16 * t);
-  }
-
   // Query blocks at or after the key tile, for each head of the group.
   const int qb_begin = k_wg0 / 32;
   const int n_qb = (L + 31) / 32 - qb_begin;
@@ -350,6 +405,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     }
   };
 
+  // Block 0's copies go out before the ordinary loads below, so the two
+  // latencies overlap.
+  issue_blk(0, 0);
+
+  // K (team 0) or V (team 1) of the pair's keys as the B operand: lane holds
+  // row `key` (rows past the end read the last row; never stored), columns
+  // 16t + 8hi .. +7.
+  f16x8 kvf[NT];
+  {
+    const f16* src = (team ? p.v : p.k) + ((size_t)(s0 + min(key, L - 1)) * p.h_kv + g) * D + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kvf[t] = *(const f16x8*)(src + 16 * t);
+  }
+
   // Per-lane LDS offsets (halves) within a block, fixed for the loop.
   int xoff[NT];  // row l32, columns 16t + 8hi (first GEMM's A operand)
 #pragma unroll
@@ -372,7 +441,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
 
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): see dq_kernel
-  issue_blk(0, 0);
   if (n_it > 1) issue_blk(1, 1);
   for (int j = 0; j <= n_it; ++j) {
     // Block j has landed for every wave (block j + 1 may still be in
@@ -511,7 +579,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.n_ktiles = (a.max_seqlen + kBK - 1) / kBK;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  const dim3 gq(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
+  // dq: persistent, at most one work-group per compute unit.
+  const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
+  const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(dq_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);

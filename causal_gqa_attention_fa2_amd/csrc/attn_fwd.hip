@@ -103,15 +103,6 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   const bool wave_has_rows = q0 < L && hig < p.G;
   const bool qvalid = qpos < L && hig < p.G;
 
-  // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7]. Rows past the
-  // sequence read its last row (loads stay unconditional) and are never stored.
-  f16x8 qf[NT];
-  {
-    const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
-  }
-
   // Copy of K/V tile kt into ring stage `stage`: instruction i of this wave
   // fills rows (wave * IPW + i) * RPI + lane / CH; lane l lands in chunk slot
   // l % CH of its row and fetches the global chunk that the swizzle maps
@@ -129,6 +120,19 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
       dma16(p.v + row + swz_tr<D>(r, slot), vdst);
     }
   };
+
+  // The first tile's copies go out before the Q loads below, so the two
+  // latencies overlap instead of adding up.
+  issue_tile(0, 0);
+
+  // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7]. Rows past the
+  // sequence read its last row (loads stay unconditional) and are never stored.
+  f16x8 qf[NT];
+  {
+    const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
+  }
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -231,8 +235,7 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   // Q^T was loaded with ordinary loads: wait for them here with the builtin
   // (whose effect the compiler tracks), so it places no wait of its own inside
   // the loop, where such a wait would also stall on the copies in flight.
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0); tile 0 included
   if (n_kt > 1) issue_tile(1, 1);
   for (int kt = 0; kt < n_kt; kt += kStages) {
     step(kt, std::integral_constant<int, 0>{});
