@@ -504,14 +504,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     f16x8 f[2];
     if (team == 0) {
-      // Causal mask on diagonal blocks, row mask on the sequence's last block.
-      const bool need_mask = kw0 + 31 > q0 || q0 + 31 >= L;
+      // Causal mask on diagonal blocks, row mask on the sequence's last
+      // block; every other block takes the unmasked copy of the loop (two
+      // copies, so the compiler does not evaluate the mask everywhere).
+      if (kw0 + 31 > q0 || q0 + 31 >= L) {
+        // Keep P where key <= row < L, i.e. 0 <= row - key < L - key.
+        const int lim = L - key;
+        const int rel = q0 + 4 * hi - key;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = q0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        float pv = fast_exp2(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
-        if (need_mask && (key > qr || qr >= L)) pv = 0.f;
-        f[i >> 3][i & 7] = (f16)pv;
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
+          const bool keep = (unsigned)(rel + 8 * (i >> 2) + (i & 3)) < (unsigned)lim;
+          f[i >> 3][i & 7] = (f16)(keep ? pv : 0.f);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          f[i >> 3][i & 7] = (f16)fast_exp2(fmaf(sa[i], p.scale_log2, -l4[i >> 2][i & 3]));
       }
       *(f16x8*)px = f[0];
       *(f16x8*)(px + 512) = f[1];

@@ -16,6 +16,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
+  int num_cus;  // compute units of the device (persistent grid)
   float scale;
 };
 
