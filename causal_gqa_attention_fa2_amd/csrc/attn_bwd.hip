@@ -9,16 +9,16 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Two kernels on one stream, no atomics, bitwise reproducible:
-//   1. dq:   query-stationary, shaped like the forward. One work-group of
-//            eight waves per (sequence, query tile, KV head, head chunk):
-//            four (head, 32-row query block) slots times two 32-key halves
-//            of each 64-key K/V tile. A wave forms its rows' D from dO and O
-//            (and stores D and LSE * log2(e) for kernel 2), then for every
-//            tile computes, on its key half, S^T = K Q^T and dP^T = V dO^T
+//   1. dq:   query-stationary, shaped like the forward. Persistent
+//            work-groups of eight waves walk work items (sequence, query
+//            tile, KV head, head chunk); each wave owns one (head, 32-row
+//            query block) slot of the item. A wave forms its rows' D from dO
+//            and O (and stores D and LSE * log2(e) for kernel 2), then for
+//            every 32-key K/V tile computes S^T = K Q^T and dP^T = V dO^T
 //            (lane = query column, so LSE and D are per-lane scalars), dS^T,
 //            and dQ^T += K^T dS^T with K^T taken by transpose reads of the
-//            same K tile. The two key halves add their partial dQ^T through
-//            LDS at the end; dq is written once, in fp16.
+//            same K tile. Each wave holds its rows' whole dQ^T, so no wave
+//            reduction follows; dq is written once, in fp16.
 //   2. dkdv: key-stationary. One work-group of eight waves per (sequence,
 //            128-key tile, KV head); waves w and w + 4 own the same 32 keys.
 //            The (G query heads) x (32-row query blocks at or after the keys)
@@ -44,7 +44,7 @@
 namespace cgqa {
 namespace {
 
-constexpr int kBC = 64;         // keys per K/V tile (dq kernel)
+constexpr int kDqBC = 32;       // keys per K/V tile (dq kernel)
 constexpr int kDqStages = 3;    // K/V ring depth (dq kernel)
 constexpr int kKvStages = 4;    // Q/dO ring depth (dkdv kernel)
 constexpr int kBK = 128;        // keys per dkdv work-group (4 x 32)
@@ -73,16 +73,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
   constexpr int CH = D / 8;    // 16-byte chunks per row
   constexpr int RPI = 64 / CH; // tile rows per copy instruction
-  constexpr int CPW = kBC * CH / 64 / 8;  // copy instructions per wave per tensor
-  static_assert(CPW >= 1 && kBC * CH == 64 * 8 * CPW, "tile must split over the waves");
-  constexpr int TILE = kBC * D;
+  constexpr int NI = kDqBC * CH / 64;  // copy instructions per tensor and tile
+  constexpr int CPW = 2 * NI / 8;       // copy instructions per wave and tile (K and V)
+  static_assert(CPW >= 1 && 2 * NI == 8 * CPW, "tile must split over the waves");
+  constexpr int TILE = kDqBC * D;
   // Ring stage st holds the K tile at smem + 2 st TILE and the V tile right
   // after it (chunk swizzle, unpadded so the copies fill them in lane order).
-  // At the end of each work item the dQ^T partials are added through stages
-  // 0 and 1 while stage 2 already receives the next item's first tile.
   __shared__ __attribute__((aligned(16))) f16 smem[2 * kDqStages * TILE];
-  static_assert(kDqStages == 3, "the item hand-over below assumes three stages");
-  static_assert(4 * ND * 16 * 64 * 4 <= 2 * 2 * TILE * 2, "reduction must fit stages 0 and 1");
+  static_assert(kDqStages == 3, "the ring below has three stages");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -91,8 +89,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   const int hi = lane >> 5;
   const int grp = lane >> 4;
   const int j16 = lane & 15;
-  const int slot = wave & 3;  // (head, query block) slot
-  const int kh = wave >> 2;   // key half of every tile
 
   // Persistent work-groups: item i is query tile n_qtiles - 1 - i / per of
   // (sequence, KV head, head chunk) i % per, so items run heaviest first.
@@ -128,10 +124,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     rem /= p.n_chunks;
     it.g = rem % p.h_kv;
     it.b = rem / p.h_kv;
-    it.s0 = p.cu[it.b];
-    it.L = p.cu[it.b + 1] - it.s0;
+    it.s0 = load_uniform(p.cu, it.b);
+    it.L = load_uniform(p.cu, it.b + 1) - it.s0;
     it.q_wg0 = qt * BR;
-    it.n_kt = it.q_wg0 < it.L ? (min(it.L, it.q_wg0 + BR) + kBC - 1) / kBC : 0;
+    it.n_kt = it.q_wg0 < it.L ? (min(it.L, it.q_wg0 + BR) + kDqBC - 1) / kDqBC : 0;
     return it;
   };
   // Next non-empty item from round r on (n_items if none).
@@ -143,41 +139,44 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     }
   };
 
-  // Copy of K/V tile kt of item `it` into ring stage st: instruction i fills
-  // tile rows i * RPI + lane / CH; lane l lands in chunk slot l % CH of its
-  // row and fetches the global chunk the swizzle maps there. Keys past the
-  // sequence fetch its last row (their scores are masked).
+  // Copy of K/V tile kt of item `it` into ring stage st: instruction i (of
+  // 2 NI) fills rows (i % NI) * RPI + lane / CH of K (i < NI) or V; lane l
+  // lands in chunk slot l % CH of its row and fetches the global chunk the
+  // swizzle maps there. Keys past the sequence fetch its last row (their
+  // scores are masked).
   auto issue_tile = [&](const Item& it, int kt, int st) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int i = wave * CPW + c;
-      const int r = i * RPI + lane / CH;
+      const int tsel = i / NI;
+      const int ii = i % NI;
+      const int r = ii * RPI + lane / CH;
       const int sl = (lane % CH) * 8;
-      const size_t row = ((size_t)(it.s0 + min(kt * kBC + r, it.L - 1)) * p.h_kv + it.g) * D;
-      f16* kst = smem + st * 2 * TILE;
-      dma16(p.k + row + swz<D>(r, sl), kst + i * 512);
-      dma16(p.v + row + swz<D>(r, sl), kst + TILE + i * 512);
+      const size_t row = ((size_t)(it.s0 + min(kt * kDqBC + r, it.L - 1)) * p.h_kv + it.g) * D;
+      dma16((tsel ? p.v : p.k) + row + swz<D>(r, sl), smem + (2 * st + tsel) * TILE + ii * 512);
     }
   };
-  // This wave's rows of item `it`.
+  // This wave's rows of item `it`: head hig of the group's chunk, 32 query
+  // positions from q0.
   struct Rows {
     int head, q0, qpos, qrow;
     bool has_rows, valid;
   };
   auto rows_of = [&](const Item& it) {
     Rows rw;
-    const int hig = it.chunk * p.hpw + slot / p.nqb;
+    const int hig = it.chunk * p.hpw + wave / p.nqb;
     rw.head = it.g * p.G + min(hig, p.G - 1);
-    rw.q0 = it.q_wg0 + (slot % p.nqb) * 32;
+    rw.q0 = it.q_wg0 + (wave % p.nqb) * 32;
     rw.qpos = rw.q0 + l32;
     rw.has_rows = rw.q0 < it.L && hig < p.G;
     rw.valid = rw.qpos < it.L && hig < p.G;
     rw.qrow = it.s0 + min(rw.qpos, it.L - 1);  // rows past the end read the last row
     return rw;
   };
-  // Q^T and dO^T as B operands (lane holds row qpos, columns 16t + 8hi .. +7)
-  // and O for the row terms.
+  // Q^T and dO^T as B operands (lane holds row qpos, columns 16t + 8hi .. +7),
+  // O for the row terms, and the row's LSE.
   f16x8 qf[NT], dof[NT], of[NT];
+  float lse_row;
   auto load_rows = [&](const Rows& rw) {
     const size_t off = ((size_t)rw.qrow * p.h_q + rw.head) * D + 8 * hi;
 #pragma unroll
@@ -186,24 +185,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       dof[t] = *(const f16x8*)(p.dout + off + 16 * t);
       of[t] = *(const f16x8*)(p.o + off + 16 * t);
     }
+    lse_row = p.lse[(size_t)rw.head * p.T + rw.qrow];
   };
 
   // Per-lane LDS offsets (halves), fixed for the kernel; the swizzle depends
   // on the row only through row % 16.
-  int koff[NT];  // K / V row 32kh + l32, columns 16t + 8hi
+  int koff[NT];  // K / V row l32, columns 16t + 8hi
 #pragma unroll
-  for (int t = 0; t < NT; ++t) koff[t] = (32 * kh + l32) * D + swz<D>(l32, 16 * t + 8 * hi);
-  // K^T transpose reads: rows 32kh + 16u + 4hi + j16/4 (and 8 further),
-  // columns 32db + 16(grp&1) + 4(j16&3); A slot e of half hi <-> key
-  // 16u + 8(e/4) + 4hi + e%4 of the wave's half, as in the dS^T B operand.
+  for (int t = 0; t < NT; ++t) koff[t] = l32 * D + swz<D>(l32, 16 * t + 8 * hi);
+  // K^T transpose reads: rows 16u + 4hi + j16/4 (and 8 further), columns
+  // 32db + 16(grp&1) + 4(j16&3); A slot e of half hi <-> key
+  // 16u + 8(e/4) + 4hi + e%4 of the tile, as in the dS^T B operand.
   int ktr0[ND], ktr1[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) {
     const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
     const int r0 = 4 * hi + (j16 >> 2);
     const int r1 = r0 + 8;
-    ktr0[db] = (32 * kh + r0) * D + swz<D>(r0, col);
-    ktr1[db] = (32 * kh + r1) * D + swz<D>(r1, col);
+    ktr0[db] = r0 * D + swz<D>(r0, col);
+    ktr1[db] = r1 * D + swz<D>(r1, col);
   }
 
   int round = 0;
@@ -215,7 +215,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   // latencies overlap instead of adding up.
   issue_tile(it, 0, 0);
   load_rows(rw);
-  int st0 = 0;  // ring stage of tile 0 of the current item
 
   for (;;) {
     float dsum = 0.f;
@@ -225,9 +224,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       for (int e = 0; e < 8; ++e) dsum += (float)dof[t][e] * (float)of[t][e];
     }
     dsum = half_swap_sum(dsum);  // D = rowsum(dO * O) over both halves of the row
-    const float lse2 = p.lse[(size_t)rw.head * p.T + rw.qrow] * kLog2e;
+    const float lse2 = lse_row * kLog2e;
 
-    f32x16 acc[ND];  // dQ^T partial over this key half: rows = head dim, cols = queries
+    f32x16 acc[ND];  // dQ^T: rows = head dim, cols = queries
 #pragma unroll
     for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
 
@@ -236,18 +235,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     // its own inside the loop; tile 1's copies go out after the wait.
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     const int n_kt = it.n_kt;
-    int st = st0;
-    if (n_kt > 1) issue_tile(it, 1, st == 2 ? 0 : st + 1);
+    int st = 0;
+    if (n_kt > 1) issue_tile(it, 1, 1);
     for (int kt = 0; kt < n_kt; ++kt) {
       // Tile kt has landed for every wave, and every wave is done with kt - 1.
-      if (kt + 1 < n_kt) wait_vm_barrier<2 * CPW>();
+      if (kt + 1 < n_kt) wait_vm_barrier<CPW>();
       else wait_vm_barrier<0>();
       if (kt + 2 < n_kt) issue_tile(it, kt + 2, st == 0 ? 2 : st - 1);
-      const int k0 = kt * kBC + 32 * kh;  // first key of this wave's half
+      const int k0 = kt * kDqBC;
       if (rw.has_rows && k0 <= rw.q0 + 31) {
         const f16* Kb = smem + st * 2 * TILE;
         const f16* Vb = Kb + TILE;
-        // S^T and dP^T for 32 keys (accumulator element i: key
+        // S^T and dP^T for the tile's 32 keys (accumulator element i: key
         // k0 + 8(i/4) + 4hi + i%4, query qpos), two interleaved chains.
         f32x16 sv = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
@@ -277,59 +276,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       st = st == 2 ? 0 : st + 1;
     }
 
-    // Every wave is done with the ring. The next item's first tile goes to
-    // stage 2 and its row loads go out now (Q, dO and O of this item are no
-    // longer needed), so their latency hides behind this item's reduction.
-    __syncthreads();
-    ++round;
-    const int nxt = next_item(round);
-    const Item it_n = nxt < n_items ? decode(nxt) : it;
-    const Rows rw_n = rows_of(it_n);
-    const bool more = nxt < n_items;
-    if (more) {
-      issue_tile(it_n, 0, 2);
-      load_rows(rw_n);
-    }
-    // Row terms for the dK/dV kernel (nothing in this kernel waits for them).
-    if (kh == 0 && rw.valid && hi == 0) {
-      p.drow[(size_t)rw.head * p.T + rw.qrow] = dsum;
-      p.lse2[(size_t)rw.head * p.T + rw.qrow] = lse2;
-    }
-    // Add the two key halves: waves 4..7 park their partials in stages 0 and
-    // 1 (lane-contiguous 16-byte groups) and waves 0..3 add them.
-    float* red = (float*)smem + slot * (ND * 16 * 64);
-    if (kh == 1) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 wv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = acc[db][4 * r4 + e];
-          *(f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4) = wv;
-        }
-      }
-    }
-    __syncthreads();
-    if (kh == 0 && rw.valid) {
+    // This wave's dq rows, scaled, in fp16; D and LSE * log2(e) for the
+    // dK/dV kernel. The stores go out before the next item's copies and row
+    // loads, so they drain first.
+    if (rw.valid) {
       f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 o2 = *(const f32x4*)(red + ((db * 4 + r4) * 64 + lane) * 4);
           f16x4 wv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = (f16)((acc[db][4 * r4 + e] + o2[e]) * p.scale);
+          for (int e = 0; e < 4; ++e) wv[e] = (f16)(acc[db][4 * r4 + e] * p.scale);
           *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = wv;
         }
       }
+      if (hi == 0) {
+        p.drow[(size_t)rw.head * p.T + rw.qrow] = dsum;
+        p.lse2[(size_t)rw.head * p.T + rw.qrow] = lse2;
+      }
     }
-    if (!more) break;
-    __syncthreads();  // stages 0 and 1 are free again before tile 1's copies
-    it = it_n;
-    rw = rw_n;
-    st0 = 2;
+    // Every wave is done with the ring (an LDS-only barrier: the stores stay
+    // in flight). The next item's first tile goes to stage 0 and its row
+    // loads go out.
+    lds_barrier();
+    ++round;
+    const int nxt = next_item(round);
+    if (nxt >= n_items) break;
+    it = decode(nxt);
+    rw = rows_of(it);
+    issue_tile(it, 0, 0);
+    load_rows(rw);
   }
 }
 
@@ -578,12 +555,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
   p.G = a.h_q / a.h_kv;
-  // dq work-groups: four (head, 32-row block) slots; hpw heads of the group
-  // (the largest power of two <= min(G, 4)) times 4 / hpw query blocks.
-  p.hpw = 1;
-  while (p.hpw * 2 <= p.G && p.hpw * 2 <= 4) p.hpw *= 2;
-  p.nqb = 4 / p.hpw;
-  p.n_chunks = (p.G + p.hpw - 1) / p.hpw;
+  // dq work items: eight (head, 32-row block) slots, one per wave; hpw heads
+  // of the group times 8 / hpw query blocks.
+  const QTileLayout lay = qtile_layout(p.G);
+  p.hpw = lay.hpw;
+  p.nqb = lay.nqb;
+  p.n_chunks = lay.n_chunks;
   p.n_qtiles = (a.max_seqlen + 32 * p.nqb - 1) / (32 * p.nqb);
   p.n_ktiles = (a.max_seqlen + kBK - 1) / kBK;
   p.scale = a.scale;

@@ -147,6 +147,22 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wave-uniform read of a read-only int32 array through the constant address
+// space, so it becomes a scalar load (waited for with lgkmcnt). A vector load
+// of the same word would be waited for with vmcnt, which also waits for every
+// copy and store of the wave still in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* a, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)a)[i];
+}
+
+// Work-group barrier that orders LDS accesses only: this wave's LDS
+// operations complete, then s_barrier. Unlike __syncthreads() it emits no
+// vmcnt(0) wait, so global loads, stores and copies still in flight stay in
+// flight across it (their consumers wait for them where they are used).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ f32x16 zero_f32x16() {
   f32x16 z;
 #pragma unroll
