@@ -122,7 +122,6 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.h_kv = dims->h_kv;
   a.head_dim = dims->head_dim;
   a.scale = scale;
-  a.num_cus = num_compute_units();
   return cgqa::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

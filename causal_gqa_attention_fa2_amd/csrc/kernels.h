@@ -16,7 +16,6 @@ struct FwdArgs {
   void* o;
   float* lse;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
-  int num_cus;  // compute units of the device (persistent grid)
   float scale;
 };
 
@@ -34,7 +33,7 @@ struct BwdArgs {
   float* drow;    // workspace: fp32 [h_q, T], rowsum(dO * O)
   float* lse2;    // workspace: fp32 [h_q, T], LSE * log2(e)
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
-  int num_cus;    // compute units of the device (persistent grids)
+  int num_cus;    // compute units of the device (persistent dq grid)
   float scale;
 };
 
