@@ -45,6 +45,10 @@ attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
   if (d->n_seqs > 0 && d->total_tokens > 0 && d->max_seqlen == 0) return ATTN_ERR_INVALID_ARG;
   // Element offsets are formed in 64-bit, token indices in 32-bit.
   if ((int64_t)d->total_tokens * d->h_q > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  // Work items (grids and item indices are 32-bit): at most one per (sequence,
+  // 32-row query block of the longest sequence, query head).
+  if ((int64_t)((d->max_seqlen + 31) / 32) * d->n_seqs * d->h_q > INT32_MAX)
+    return ATTN_ERR_UNSUPPORTED;
   *empty = d->n_seqs == 0 || d->total_tokens == 0;
   return ATTN_OK;
 }

@@ -49,7 +49,10 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer  */
     ATTN_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, group size above 16,
-                                 block size not 16                           */
+                                 block size not 16, or a batch too large for
+                                 32-bit indexing: total_tokens * h_q or
+                                 ceil(max_seqlen / 32) * n_seqs * h_q above
+                                 INT32_MAX                                   */
     ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required  */
     ATTN_ERR_HIP = 4          /* the HIP runtime reported a launch error     */
 } attn_status;

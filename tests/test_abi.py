@@ -63,6 +63,10 @@ def test_fwd_argument_checks(lib):
         assert _fwd(lib, VarlenDims(**d)) == code, (field, bad)
     d = dict(good, h_q=17 * 2, h_kv=2)  # group of 17 query heads
     assert _fwd(lib, VarlenDims(**d)) == UNSUPPORTED
+    # A batch whose work-item grid would not fit 32 bits: one long sequence
+    # next to millions of one-token sequences.
+    d = dict(good, n_seqs=2_000_000, total_tokens=4_000_000, max_seqlen=2_000_001)
+    assert _fwd(lib, VarlenDims(**d)) == UNSUPPORTED
     dims = VarlenDims(**good)
     assert _fwd(lib, dims, q=0) == INVALID
     assert _fwd(lib, dims, lse=0) == INVALID
