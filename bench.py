@@ -257,7 +257,7 @@ def main():
                 "GB/s": round(b_bwd / t_bwd / 1e9, 1), "launches": 2},
         "decode": {"us": round(t_dec * 1e6, 2), "GB/s": round(dec_gbps, 1),
                    "hbm_peak_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "alg_bytes": int(b_dec), "launches": 2},
+                   "alg_bytes": int(b_dec), "launches": 3},
         "roofline": roofline,
         "source_digest": source_digest(),
     }
