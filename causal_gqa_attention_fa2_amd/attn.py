@@ -108,6 +108,25 @@ def _check(fn, status):
         raise AttnError(fn, status)
 
 
+def debug_validate_enabled():
+    """ATTN_DEBUG_VALIDATE=1: before every launch, copy the device index
+    arrays to the host (synchronously) and check their contents with the
+    library's host validators. Off by default: the library itself never
+    reads them on the host."""
+    return os.environ.get("ATTN_DEBUG_VALIDATE", "") == "1"
+
+
+def validate_varlen(dims, cu_seqlens):
+    """Raise AttnError unless cu_seqlens (any device) is valid for dims."""
+    _check("attn_check_cu_seqlens", check_cu_seqlens_host(dims, cu_seqlens.cpu()))
+
+
+def validate_paged(dims, block_table, ctx_lens):
+    """Raise AttnError unless block_table and ctx_lens (any device) are valid
+    for dims."""
+    _check("attn_check_paged", check_paged_host(dims, block_table.cpu(), ctx_lens.cpu()))
+
+
 def varlen_dims(q, k, cu_seqlens, max_seqlen=None):
     T, h_q, d = q.shape
     if max_seqlen is None:  # host copy: synchronises, meant for tests
@@ -138,6 +157,8 @@ def fwd(q, k, v, cu_seqlens, scale=None, o=None, lse=None, max_seqlen=None):
     if o.shape != q.shape or lse.shape != (h_q, T):
         raise ValueError("o / lse shape mismatch")
     dims = varlen_dims(q, k, cu_seqlens, max_seqlen)
+    if debug_validate_enabled():
+        validate_varlen(dims, cu_seqlens)
     _check("attn_fwd", lib.attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(cu_seqlens), float(scale), _ptr(o), _ptr(lse),
                                     _stream()))
@@ -173,6 +194,8 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
         raise ValueError("gradient shape mismatch")
     dims = varlen_dims(q, k, cu_seqlens, max_seqlen)
+    if debug_validate_enabled():
+        validate_varlen(dims, cu_seqlens)
     need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -217,6 +240,8 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, scale=None, o=None,
     if o.shape != q.shape:
         raise ValueError("o shape mismatch")
     dims = paged_dims(q, k_pool, block_table, max_ctx_len)
+    if debug_validate_enabled():
+        validate_paged(dims, block_table, ctx_lens)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

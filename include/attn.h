@@ -165,7 +165,12 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status status);
 
-/* Host-side check of a HOST copy of cu_seqlens against dims: cu[0] == 0,
+/* The entry points above do not read the contents of the device index
+ * arrays on the host (they never synchronize). The two validators below check
+ * host copies; the Python binding runs them before every launch when the
+ * environment sets ATTN_DEBUG_VALIDATE=1 (a synchronous debug mode).
+ *
+ * Host-side check of a HOST copy of cu_seqlens against dims: cu[0] == 0,
  * non-decreasing, cu[n] == total_tokens, every length <= max_seqlen.
  * Returns ATTN_OK or ATTN_ERR_INVALID_ARG. Makes no HIP call. */
 attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu_host);

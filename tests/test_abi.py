@@ -143,6 +143,24 @@ def test_host_validators():
     assert A.attn.check_paged_host(pd, bt, torch.tensor([0, 0])) == OK
 
 
+def test_debug_validate_helpers(monkeypatch):
+    """The checks ATTN_DEBUG_VALIDATE=1 runs before each launch raise on bad
+    index contents (host tensors here; the binding copies device ones)."""
+    monkeypatch.delenv("ATTN_DEBUG_VALIDATE", raising=False)
+    assert not A.attn.debug_validate_enabled()
+    monkeypatch.setenv("ATTN_DEBUG_VALIDATE", "1")
+    assert A.attn.debug_validate_enabled()
+    dims = VarlenDims(3, 10, 7, 4, 2, 64)
+    A.attn.validate_varlen(dims, torch.tensor([0, 3, 3, 10], dtype=torch.int32))
+    with pytest.raises(A.attn.AttnError):
+        A.attn.validate_varlen(dims, torch.tensor([0, 3, 3, 9], dtype=torch.int32))
+    pd = PagedDims(2, 4, 2, 64, 16, 3, 5, 40)
+    bt = torch.tensor([[4, 0, -1], [1, 2, 3]], dtype=torch.int32)
+    A.attn.validate_paged(pd, bt, torch.tensor([17, 40], dtype=torch.int32))
+    with pytest.raises(A.attn.AttnError):
+        A.attn.validate_paged(pd, bt, torch.tensor([33, 40], dtype=torch.int32))
+
+
 def test_binding_rejects_host_tensors():
     q = torch.zeros(4, 2, 64, dtype=torch.float16)
     k = torch.zeros(4, 1, 64, dtype=torch.float16)
