@@ -32,7 +32,9 @@
 //   O^T += V^T P^T   32x32x16 MFMA; P^T feeds the B operand straight from
 //                    the S^T accumulators; V^T is read from the row-major V
 //                    tile with ds_read_b64_tr_b16.
-// The O rescale is skipped when no row maximum of the wave grew (alpha = 1).
+// The softmax reference point m moves only when some row's maximum passes it
+// by more than 2^8 in weight, so O is rescaled in few tiles (with random data
+// almost only the first), not whenever any of the wave's 32 row maxima grows.
 #include "cdna4.h"
 #include "kernels.h"
 
@@ -43,6 +45,7 @@ namespace cgqa {
 namespace {
 
 constexpr int kBC = 64;                // keys per tile
+constexpr float kLazy = 8.f;           // headroom (log2 units) of the softmax reference
 constexpr int kStages = 3;             // LDS ring depth
 constexpr int kNTH = 64 * kQWaves;     // threads per work-group
 
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   f32x16 oacc[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) oacc[db] = zero_f32x16();
-  float m_run = kMaxInit;  // running max of the scaled scores (log2 units)
+  float m_run = kMaxInit;  // reference maximum of the scaled scores (log2 units)
   float l_run = 0.f;       // this half-wave's share of the row sum
 
   // Per-lane LDS offsets (halves) of the operand reads, fixed for the whole
@@ -189,9 +192,14 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
     mx = half_swap_max(mx) * p.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    // Rescale only when some row's maximum grew (alpha == 1 otherwise).
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+    // m_run is a reference point, not always the exact running maximum: it
+    // moves (and O and l are rescaled) only when a row's maximum passes it by
+    // more than kLazy, so the weights below stay <= 2^kLazy and the wave
+    // skips the rescale in almost every tile after the first. The result is
+    // the same softmax up to rounding, whatever the reference.
+    const bool grow = mx > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -199,8 +207,9 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_new = m_run;
 
     // P^T = exp2(S^T * scale * log2(e) - m), as B operands: k-step u covers
     // tile keys 16u..16u+15; slot e of half hi holds key 16u + 8(e/4) +
