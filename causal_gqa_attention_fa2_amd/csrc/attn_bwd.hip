@@ -41,6 +41,8 @@
 #include "cdna4.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace cgqa {
 namespace {
 
@@ -235,45 +237,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     // its own inside the loop; tile 1's copies go out after the wait.
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     const int n_kt = it.n_kt;
-    int st = 0;
     if (n_kt > 1) issue_tile(it, 1, 1);
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // One tile step on ring stage S = kt % 3 (a compile-time constant, so
+    // every LDS operand address is a per-lane offset plus an immediate); the
+    // copies of tile kt + 2 go to stage (S + 2) % 3, which held tile kt - 1.
+    auto step = [&](int kt, auto S) __attribute__((always_inline)) {
+      constexpr int st = decltype(S)::value;
       // Tile kt has landed for every wave, and every wave is done with kt - 1.
       if (kt + 1 < n_kt) wait_vm_barrier<CPW>();
       else wait_vm_barrier<0>();
-      if (kt + 2 < n_kt) issue_tile(it, kt + 2, st == 0 ? 2 : st - 1);
+      if (kt + 2 < n_kt) issue_tile(it, kt + 2, (st + 2) % kDqStages);
       const int k0 = kt * kDqBC;
-      if (rw.has_rows && k0 <= rw.q0 + 31) {
-        const f16* Kb = smem + st * 2 * TILE;
-        const f16* Vb = Kb + TILE;
-        // S^T and dP^T for the tile's 32 keys (accumulator element i: key
-        // k0 + 8(i/4) + 4hi + i%4, query qpos), two interleaved chains.
-        f32x16 sv = zero_f32x16(), dp = zero_f32x16();
+      if (!rw.has_rows || k0 > rw.q0 + 31) return;  // fully masked for this wave
+      const f16* Kb = smem + st * 2 * TILE;
+      const f16* Vb = Kb + TILE;
+      // S^T and dP^T for the tile's 32 keys (accumulator element i: key
+      // k0 + 8(i/4) + 4hi + i%4, query qpos), two interleaved chains.
+      f32x16 sv = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          sv = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], sv);
-          dp = mfma32x32x16(*(const f16x8*)(Vb + koff[t]), dof[t], dp);
-        }
-        const bool diag = k0 + 31 > rw.q0;
-        f16x8 dsf[2];
+      for (int t = 0; t < NT; ++t) {
+        sv = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], sv);
+        dp = mfma32x32x16(*(const f16x8*)(Vb + koff[t]), dof[t], dp);
+      }
+      f16x8 dsf[2];
+      if (k0 + 31 > rw.q0) {
+        // Diagonal tile: keep P where key <= qpos, i.e. the constant part
+        // 8(i/4) + i%4 of the key is <= qpos - k0 - 4hi.
+        const int lim = rw.qpos - k0 - 4 * hi;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
-          if (diag && k0 + 8 * (i >> 2) + 4 * hi + (i & 3) > rw.qpos) pv = 0.f;
+          if (8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
           dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
         }
-        // dQ^T += K^T dS^T over the 32 keys (K^T by transpose reads).
+      } else {
+        // Every other tile takes this unmasked copy (two copies, so the
+        // compiler does not evaluate the mask everywhere).
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const f16x8 kt = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
-                                  lds_read_tr(Kb + ktr1[db] + 16 * u * D));
-            acc[db] = mfma32x32x16(kt, dsf[u], acc[db]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
+          dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
         }
       }
-      st = st == 2 ? 0 : st + 1;
+      // dQ^T += K^T dS^T over the 32 keys (K^T by transpose reads).
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const f16x8 kt = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
+                                lds_read_tr(Kb + ktr1[db] + 16 * u * D));
+          acc[db] = mfma32x32x16(kt, dsf[u], acc[db]);
+        }
+      }
+    };
+    for (int kt = 0; kt < n_kt; kt += kDqStages) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
     }
 
     // This wave's dq rows, scaled, in fp16; D and LSE * log2(e) for the
