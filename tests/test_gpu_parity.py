@@ -39,6 +39,37 @@ def test_fwd_bwd_edge_lengths(gpu, h_q, h_kv, d):
     check_bwd(name, inp, dq, dk, dv)
 
 
+def _random_cases(n, seed):
+    """Seeded random varlen batches: 1-5 sequences of 0-400 tokens, KV heads
+    1-4, group size 1-8 (including non powers of two) and d 64 or 128."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        lens = [int(x) for x in g.integers(0, 401, size=int(g.integers(1, 6)))]
+        h_kv = int(g.choice([1, 2, 4]))
+        G = int(g.choice([1, 2, 3, 4, 5, 8]))
+        d = int(g.choice([64, 128]))
+        cases.append((lens, G * h_kv, h_kv, d, 3000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("lens,h_q,h_kv,d,seed", _random_cases(10, 77),
+                         ids=lambda x: str(x))
+def test_random_shapes(gpu, lens, h_q, h_kv, d, seed):
+    """Forward and backward on random ragged batches, every sequence and KV
+    group compared with the oracle."""
+    name = f"random {lens} hq{h_q} hkv{h_kv} d{d}"
+    inp = W.make_train_inputs(lens, h_q, h_kv, d, seed=seed)
+    if inp["total_tokens"] == 0:
+        pytest.skip("empty batch (covered by the zero-length test)")
+    dd = dev(inp, gpu)
+    o, lse = gpu_fwd(dd)
+    dq, dk, dv = gpu_bwd(dd, o, lse)
+    torch.cuda.synchronize()
+    check_fwd(name, inp, o, lse)
+    check_bwd(name, inp, dq, dk, dv)
+
+
 def test_tiny_workload(gpu):
     inp = W.workload_inputs("tiny")
     dd = dev(inp, gpu)
