@@ -259,6 +259,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
         sv = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], sv);
         dp = mfma32x32x16(*(const f16x8*)(Vb + koff[t]), dof[t], dp);
       }
+      // K^T fragments of the dQ product, read while the softmax terms below
+      // are computed.
+      f16x8 ktf[2][ND];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          ktf[u][db] = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
+                            lds_read_tr(Kb + ktr1[db] + 16 * u * D));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f16x8 dsf[2];
       if (k0 + 31 > rw.q0) {
         // Diagonal tile: keep P where key <= qpos, i.e. the constant part
@@ -283,11 +294,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const f16x8 kt = cat4(lds_read_tr(Kb + ktr0[db] + 16 * u * D),
-                                lds_read_tr(Kb + ktr1[db] + 16 * u * D));
-          acc[db] = mfma32x32x16(kt, dsf[u], acc[db]);
-        }
+        for (int db = 0; db < ND; ++db) acc[db] = mfma32x32x16(ktf[u][db], dsf[u], acc[db]);
       }
     };
     for (int kt = 0; kt < n_kt; kt += kDqStages) {

@@ -171,12 +171,35 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     const f16* Kb = Ks[stage];
     const f16* Vb = Vs[stage];
     // S^T for the two 32-key halves of the tile, as two interleaved chains.
+    // Every K fragment of the tile is read in one batch before the products
+    // (scheduling fences keep the compiler from pairing each read with its
+    // use, which left the matrix core waiting on LDS latency), and the V^T
+    // fragments go out right behind them, so they land during the softmax.
     f32x16 s[2] = {zero_f32x16(), zero_f32x16()};
+    {
+      f16x8 kf[2][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      s[0] = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], s[0]);
-      s[1] = mfma32x32x16(*(const f16x8*)(Kb + 32 * D + koff[t]), qf[t], s[1]);
+      for (int t = 0; t < NT; ++t) {
+        kf[0][t] = *(const f16x8*)(Kb + koff[t]);
+        kf[1][t] = *(const f16x8*)(Kb + 32 * D + koff[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s[0] = mfma32x32x16(kf[0][t], qf[t], s[0]);
+        s[1] = mfma32x32x16(kf[1][t], qf[t], s[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    f16x8 vf[4][ND];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        vf[u][db] = cat4(lds_read_tr(Vb + voff[db] + 16 * u * D),
+                         lds_read_tr(Vb + voff[db] + (16 * u + 8) * D));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // Causal mask (diagonal tiles only) and the tile maximum of raw scores.
     if (kt * kBC + kBC - 1 > q0) {
 #pragma unroll
@@ -228,16 +251,13 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     l_run += rs;
 
     // O^T += V^T P^T. A-operand slot e of half hi must hold V[key(e)][d]
-    // for the same keys: transpose reads of rows 16u + 4hi + j16/4 and 8
-    // rows further.
+    // for the same keys: transpose reads (above) of rows 16u + 4hi + j16/4
+    // and 8 rows further. The k-step loop is outermost, so consecutive
+    // products go to different accumulators (four independent chains).
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f16x4 lo = lds_read_tr(Vb + voff[db] + 16 * u * D);
-        const f16x4 up = lds_read_tr(Vb + voff[db] + (16 * u + 8) * D);
-        oacc[db] = mfma32x32x16(cat4(lo, up), pf[u], oacc[db]);
-      }
+      for (int db = 0; db < ND; ++db) oacc[db] = mfma32x32x16(vf[u][db], pf[u], oacc[db]);
     }
   };
 
