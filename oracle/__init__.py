@@ -18,6 +18,9 @@ of masked softmax attention, evaluated naively in float64:
   on O only.
 * ``attn_decode_ref`` -- one query token per sequence attending to its whole
   context held in a paged key/value pool.
+* ``kv_append_ref`` and ``attn_prefill_ref`` -- the rollout engine's chunked
+  prefill: new tokens written into the paged pool, then causal attention of
+  the new queries against the whole paged context.
 
 Every function is pinned by tests that do not re-use its formulas: closed
 forms, invariants, finite differences, a hand-derived worked example and
@@ -27,5 +30,7 @@ from .attention import (  # noqa: F401
     attn_fwd_ref,
     attn_bwd_ref,
     attn_decode_ref,
+    attn_prefill_ref,
+    kv_append_ref,
     kv_head_of,
 )

@@ -190,3 +190,97 @@ def attn_decode_ref(q, k_pool, v_pool, block_table, ctx_lens, scale):
             w = np.exp(s - s.max())
             o[b, h] = (w / w.sum()) @ V[:, g]
     return o
+
+
+# ----------------------------------------------------------------------------- paged prefill
+#
+# The rollout engine's other attention call (pitchhut "Key Features", item 2:
+# continuous batching over a paged key/value cache; mlllm.io "What happened"):
+# a chunk of new tokens of each sequence is appended to the cache and attends
+# causally to the whole cached context. Readings of points the pages leave
+# open: ``ctx_lens[b]`` counts the context INCLUDING the sequence's new tokens,
+# which are its last q_len_b = cu_q[b+1] - cu_q[b] positions; new token i of
+# sequence b therefore sits at context position ctx_b - q_len_b + i and sees
+# positions 0 .. ctx_b - q_len_b + i.
+
+
+def _chunk_offset(ctx, q_len):
+    """Context position of a sequence's first new token (its new tokens are
+    the last ``q_len`` of its ``ctx`` positions)."""
+    if q_len < 0 or q_len > ctx:
+        raise ValueError("a chunk cannot be longer than its context")
+    return ctx - q_len
+
+
+def kv_append_ref(k_pool, v_pool, k_new, v_new, cu_q, block_table, ctx_lens):
+    """Write each sequence's new keys and values into the paged pools.
+
+    k_new, v_new [Tq, H_kv, d] packed by ``cu_q``; new token i of sequence b
+    goes to context position t = ctx_b - q_len_b + i, i.e. slot t % bs of
+    physical block block_table[b][t // bs]. Returns new (k_pool, v_pool)
+    arrays (copies, input dtype); every other slot is left as it was.
+    """
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    k_new = np.asarray(k_new)
+    v_new = np.asarray(v_new)
+    cu = np.asarray(cu_q, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    bs = kp.shape[1]
+    for b in range(len(cu) - 1):
+        s0, e0 = int(cu[b]), int(cu[b + 1])
+        c = int(ctx[b])
+        off = _chunk_offset(c, e0 - s0)
+        phys, slot = _paged_positions(bt[b], c, bs)
+        phys, slot = phys[off:], slot[off:]
+        if np.any(phys < 0) or np.any(phys >= kp.shape[0]):
+            raise ValueError("block_table entry out of range")
+        kp[phys, slot] = k_new[s0:e0]
+        vp[phys, slot] = v_new[s0:e0]
+    return kp, vp
+
+
+def attn_prefill_ref(q, k_pool, v_pool, block_table, ctx_lens, cu_q, scale):
+    """Causal GQA attention of new query tokens against a paged context.
+
+    q [Tq, H_q, d] packed by ``cu_q``; pools [num_blocks, bs, H_kv, d];
+    ``ctx_lens`` include the new tokens. New token i of sequence b (context
+    position p = ctx_b - q_len_b + i) attends to context positions 0..p,
+    gathered from the pools; S, LSE and O as in ``attn_fwd_ref``. Returns
+    (o [Tq, H_q, d], lse [H_q, Tq]) in float64.
+    """
+    q = _f64(q)
+    k_pool = np.asarray(k_pool)
+    v_pool = np.asarray(v_pool)
+    cu = np.asarray(cu_q, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    Tq, h_q, d = q.shape
+    nb, bs, h_kv, d2 = k_pool.shape
+    if d2 != d or v_pool.shape != k_pool.shape or h_q % h_kv:
+        raise ValueError("pool / query shapes disagree")
+    if cu.ndim != 1 or cu[0] != 0 or cu[-1] != Tq or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_q must rise from 0 to Tq")
+    o = np.zeros((Tq, h_q, d))
+    lse = np.zeros((h_q, Tq))
+    for b in range(len(cu) - 1):
+        s0, e0 = int(cu[b]), int(cu[b + 1])
+        if e0 == s0:
+            continue
+        c = int(ctx[b])
+        off = _chunk_offset(c, e0 - s0)
+        phys, slot = _paged_positions(bt[b], c, bs)
+        if np.any(phys < 0) or np.any(phys >= nb):
+            raise ValueError("block_table entry out of range")
+        K = _f64(k_pool[phys, slot])  # [c, H_kv, d]
+        V = _f64(v_pool[phys, slot])
+        for h in range(h_q):
+            g = kv_head_of(h, h_q, h_kv)
+            for r0 in range(0, e0 - s0, ROW_CHUNK):
+                r1 = min(e0 - s0, r0 + ROW_CHUNK)
+                s = _masked_scores(q[s0 + r0:s0 + r1, h], K[:off + r1, g], off + r0, scale)
+                p, lse_rows = _softmax_rows(s)
+                o[s0 + r0:s0 + r1, h] = p @ V[:off + r1, g]
+                lse[h, s0 + r0:s0 + r1] = lse_rows
+    return o, lse
