@@ -1,22 +1,28 @@
 """Causal grouped-query attention for MI355X (gfx950).
 
 FlashAttention-2-style forward and backward over packed variable-length
-fp16 sequences and a paged-KV single-token decode, as hand-written HIP
-kernels behind the C ABI declared in include/attn.h. ``fwd``, ``bwd`` and
-``decode_paged`` are thin ctypes wrappers of attn_fwd, attn_bwd and
-attn_decode_paged; the shared library is loaded on first use and every call
-raises if it is missing.
+fp16 sequences, a paged-KV single-token decode, and the chunked prefill over
+the paged cache (key/value append plus causal attention of the new tokens),
+as hand-written HIP kernels behind the C ABI declared in include/attn.h.
+``fwd``, ``bwd``, ``decode_paged``, ``kv_append`` and ``prefill_paged`` are
+thin ctypes wrappers of attn_fwd, attn_bwd, attn_decode_paged,
+attn_kv_append and attn_prefill_paged; the shared library is loaded on first
+use and every call raises if it is missing.
 """
 from .attn import (  # noqa: F401
     AttnError,
     PagedDims,
+    PrefillDims,
     VarlenDims,
     bwd,
     bwd_workspace_bytes,
     decode_paged,
     decode_workspace_bytes,
     fwd,
+    kv_append,
     load_library,
     paged_dims,
+    prefill_dims,
+    prefill_paged,
     varlen_dims,
 )

@@ -21,8 +21,9 @@ ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
                 3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
-            "attn_decode_workspace_bytes", "attn_status_string", "attn_check_cu_seqlens",
-            "attn_check_paged")
+            "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
+            "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
+            "attn_check_prefill")
 
 
 class AttnError(RuntimeError):
@@ -42,6 +43,11 @@ class PagedDims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_ctx_len", ctypes.c_int32)]
+
+
+class PrefillDims(ctypes.Structure):
+    _fields_ = [("paged", PagedDims), ("total_q", ctypes.c_int32),
+                ("max_q_len", ctypes.c_int32)]
 
 
 _LIB = None
@@ -76,6 +82,14 @@ def load_library():
     lib.attn_check_cu_seqlens.restype = ctypes.c_int
     lib.attn_check_paged.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp]
     lib.attn_check_paged.restype = ctypes.c_int
+    lib.attn_kv_append.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp]
+    lib.attn_kv_append.restype = ctypes.c_int
+    lib.attn_prefill_paged.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, ctypes.c_float, _vp]
+    lib.attn_prefill_paged.restype = ctypes.c_int
+    lib.attn_check_prefill.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp]
+    lib.attn_check_prefill.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -265,3 +279,99 @@ def check_paged_host(dims, block_table_host, ctx_host):
     cx = ctx_host.to(torch.int32).contiguous()
     return int(load_library().attn_check_paged(ctypes.byref(dims), _vp(bt.data_ptr()),
                                                _vp(cx.data_ptr())))
+
+
+def prefill_dims(q_or_knew, k_pool, block_table, cu_q, max_ctx_len, max_q_len=None):
+    """PrefillDims of a chunked prefill; host copies of max_ctx_len and (if
+    not given) max_q_len size the launch."""
+    n = cu_q.numel() - 1
+    nb, bs, h_kv, d = k_pool.shape
+    h = q_or_knew.shape[1]
+    if max_q_len is None:  # host copy: synchronises, meant for tests
+        cu = cu_q.cpu()
+        max_q_len = int((cu[1:] - cu[:-1]).max()) if n > 0 else 0
+    return PrefillDims(PagedDims(n, h, h_kv, d, bs, block_table.shape[1], nb, int(max_ctx_len)),
+                       q_or_knew.shape[0], int(max_q_len))
+
+
+def validate_prefill(dims, cu_q, block_table, ctx_lens):
+    """Raise AttnError unless cu_q, block_table and ctx_lens (any device) are
+    valid for dims."""
+    _check("attn_check_prefill", check_prefill_host(dims, cu_q.cpu(), block_table.cpu(),
+                                                    ctx_lens.cpu()))
+
+
+def _prefill_args(k_pool, v_pool, block_table, ctx_lens, cu_q, dev):
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    _need(cu_q, "cu_q", torch.int32, 1, dev)
+    n = cu_q.numel() - 1
+    if k_pool.shape != v_pool.shape or block_table.shape[0] != n or ctx_lens.shape[0] != n:
+        raise ValueError("shape mismatch")
+
+
+def kv_append(k_new, v_new, cu_q, block_table, ctx_lens, k_pool, v_pool, max_ctx_len=None,
+              max_q_len=None):
+    """attn_kv_append: writes the new keys/values into k_pool / v_pool in place."""
+    lib = load_library()
+    dev = k_new.device
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3, dev)
+    _prefill_args(k_pool, v_pool, block_table, ctx_lens, cu_q, dev)
+    if k_new.shape != v_new.shape or k_new.shape[1:] != k_pool.shape[2:]:
+        raise ValueError("k_new, v_new must be [total_q, h_kv, d] matching the pools")
+    if max_ctx_len is None:  # host copy: synchronises, meant for tests
+        max_ctx_len = int(ctx_lens.max()) if ctx_lens.numel() else 0
+    dims = prefill_dims(k_new, k_pool, block_table, cu_q, max_ctx_len, max_q_len)
+    if debug_validate_enabled():
+        validate_prefill(dims, cu_q, block_table, ctx_lens)
+    _check("attn_kv_append",
+           lib.attn_kv_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cu_q),
+                              _ptr(block_table), _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool),
+                              _stream()))
+    return k_pool, v_pool
+
+
+def prefill_paged(q, k_pool, v_pool, block_table, ctx_lens, cu_q, scale=None, o=None, lse=None,
+                  with_lse=True, max_ctx_len=None, max_q_len=None):
+    """attn_prefill_paged: returns (o fp16 [total_q, h_q, d], lse fp32 [h_q, total_q] or None)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.float16, 3)
+    _prefill_args(k_pool, v_pool, block_table, ctx_lens, cu_q, dev)
+    Tq, h_q, d = q.shape
+    if k_pool.shape[3] != d:
+        raise ValueError("q and the pools disagree on head_dim")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if max_ctx_len is None:  # host copy: synchronises, meant for tests
+        max_ctx_len = int(ctx_lens.max()) if ctx_lens.numel() else 0
+    o = torch.empty_like(q) if o is None else o
+    _need(o, "o", torch.float16, 3, dev)
+    if o.shape != q.shape:
+        raise ValueError("o shape mismatch")
+    if with_lse and lse is None:
+        lse = torch.empty((h_q, Tq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if lse.shape != (h_q, Tq):
+            raise ValueError("lse shape mismatch")
+    dims = prefill_dims(q, k_pool, block_table, cu_q, max_ctx_len, max_q_len)
+    if debug_validate_enabled():
+        validate_prefill(dims, cu_q, block_table, ctx_lens)
+    _check("attn_prefill_paged",
+           lib.attn_prefill_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                  _ptr(block_table), _ptr(ctx_lens), _ptr(cu_q), _ptr(o),
+                                  _ptr(lse), float(scale), _stream()))
+    return o, lse
+
+
+def check_prefill_host(dims, cu_host, block_table_host, ctx_host):
+    """attn_check_prefill on host int32 tensors."""
+    cu = cu_host.to(torch.int32).contiguous()
+    bt = block_table_host.to(torch.int32).contiguous()
+    cx = ctx_host.to(torch.int32).contiguous()
+    return int(load_library().attn_check_prefill(ctypes.byref(dims), _vp(cu.data_ptr()),
+                                                 _vp(bt.data_ptr()), _vp(cx.data_ptr())))

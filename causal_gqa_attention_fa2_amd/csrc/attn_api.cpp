@@ -87,6 +87,27 @@ size_t decode_ws_parts(const attn_paged_dims* d, size_t* o_bytes, size_t* ml_byt
   return *o_bytes + *ml_bytes + align_up((size_t)(d->n_seqs + 1 + nwg) * sizeof(int32_t));
 }
 
+// Shape checks of a chunked prefill: the pool side as for the decode, then
+// the packed new tokens. Sets *empty when there is nothing to compute.
+attn_status check_prefill(const attn_prefill_dims* d, bool* empty) {
+  if (!d) return ATTN_ERR_INVALID_ARG;
+  bool no_seqs = false;
+  const attn_status st = check_paged(&d->paged, &no_seqs);
+  if (st != ATTN_OK) return st;
+  if (d->total_q < 0 || d->max_q_len < 0 || d->max_q_len > d->total_q) return ATTN_ERR_INVALID_ARG;
+  if (d->max_q_len > d->paged.max_ctx_len) return ATTN_ERR_INVALID_ARG;
+  if (no_seqs && d->total_q > 0) return ATTN_ERR_INVALID_ARG;
+  if (d->total_q > 0 && d->max_q_len == 0) return ATTN_ERR_INVALID_ARG;
+  // 32-bit indices: LSE rows, work items and block-table entries.
+  if ((int64_t)d->total_q * d->paged.h_q > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)((d->max_q_len + 31) / 32) * d->paged.n_seqs * d->paged.h_q > INT32_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)d->paged.n_seqs * d->paged.max_blocks_per_seq > INT32_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  *empty = no_seqs || d->total_q == 0;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +239,87 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
   a.n_wgs = cgqa::decode_num_wgs(dims->n_seqs, dims->max_ctx_len);
   a.scale = scale;
   return cgqa::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_kv_append(const attn_prefill_dims* dims, const void* k_new, const void* v_new,
+                           const int32_t* cu_q, const int32_t* block_table,
+                           const int32_t* ctx_lens, void* k_pool, void* v_pool, void* stream) {
+  bool empty = false;
+  attn_status st = check_prefill(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!k_new || !v_new || !cu_q || !block_table || !ctx_lens || !k_pool || !v_pool)
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)cu_q & 3u) || ((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_new = cu_q;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.n_seqs = dims->paged.n_seqs;
+  a.max_new = dims->max_q_len;
+  a.h_kv = dims->paged.h_kv;
+  a.head_dim = dims->paged.head_dim;
+  a.max_blocks_per_seq = dims->paged.max_blocks_per_seq;
+  a.num_blocks = dims->paged.num_blocks;
+  a.max_ctx_len = dims->paged.max_ctx_len;
+  return cgqa::launch_kv_append(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* ctx_lens, const int32_t* cu_q, void* o,
+                               float* lse, float scale, void* stream) {
+  bool empty = false;
+  attn_status st = check_prefill(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !cu_q || !o)
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
+      !aligned16(lse) || ((uintptr_t)cu_q & 3u) || ((uintptr_t)block_table & 3u) ||
+      ((uintptr_t)ctx_lens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::FwdArgs a;
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.cu_seqlens = cu_q;
+  a.o = o;
+  a.lse = lse;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.max_blocks_per_seq = dims->paged.max_blocks_per_seq;
+  a.num_blocks = dims->paged.num_blocks;
+  a.max_ctx_len = dims->paged.max_ctx_len;
+  a.n_seqs = dims->paged.n_seqs;
+  a.total_tokens = dims->total_q;
+  a.max_seqlen = dims->max_q_len;
+  a.h_q = dims->paged.h_q;
+  a.h_kv = dims->paged.h_kv;
+  a.head_dim = dims->paged.head_dim;
+  a.scale = scale;
+  return cgqa::launch_prefill(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_check_prefill(const attn_prefill_dims* dims, const int32_t* cu,
+                               const int32_t* table, const int32_t* ctx) {
+  bool empty = false;
+  if (check_prefill(dims, &empty) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const int32_t n = dims->paged.n_seqs;
+  if (!cu || (n > 0 && !ctx)) return ATTN_ERR_INVALID_ARG;
+  if (n > 0 && attn_check_paged(&dims->paged, table, ctx) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (cu[0] != 0 || cu[n] != dims->total_q) return ATTN_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < n; ++b) {
+    const int32_t len = cu[b + 1] - cu[b];
+    if (len < 0 || len > dims->max_q_len || len > ctx[b]) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
 }
 
 attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu) {

@@ -1,0 +1,76 @@
+// attn_cache.hip -- key/value cache append for the chunked prefill over a
+// paged cache (the rollout engine's "paged key-value caching"; pitchhut "Key
+// Features", item 2).
+//
+// New token i of sequence b (row cu[b] + i of k_new / v_new) is the context
+// position t = ctx[b] - L_b + i (L_b = cu[b+1] - cu[b], the sequence's new
+// tokens are the last L_b of its ctx[b] positions) and goes to slot t % 16
+// of pool block bt[b][t / 16]. Pure data movement, bound by HBM: each
+// work-group moves 16 tokens of one sequence in 16-byte pieces, every byte
+// read once and written once.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace cgqa {
+namespace {
+
+constexpr int kTokPerWG = 16;
+constexpr int kAppendThreads = 256;
+
+struct AppendParams {
+  const uint4* __restrict__ k_new;
+  const uint4* __restrict__ v_new;
+  const int32_t* __restrict__ cu;
+  const int32_t* __restrict__ bt;
+  const int32_t* __restrict__ ctx;
+  uint4* __restrict__ k_pool;
+  uint4* __restrict__ v_pool;
+  int cpt;  // 16-byte pieces per token row (h_kv * d / 8)
+  int max_blocks, num_blocks, max_ctx;
+};
+
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams p) {
+  const int b = blockIdx.y;
+  const int s0 = p.cu[b];
+  const int L = p.cu[b + 1] - s0;
+  const int c = min(p.ctx[b], p.max_ctx);  // a context past the table is clamped
+  const int i0 = blockIdx.x * kTokPerWG;
+  if (i0 >= L || c < L) return;  // nothing here, or an invalid batch
+  const int off = c - L;
+  const int n = min(kTokPerWG, L - i0) * p.cpt;
+  for (int e = threadIdx.x; e < n; e += kAppendThreads) {
+    const int tok = e / p.cpt;
+    const int piece = e - tok * p.cpt;
+    const int i = i0 + tok;
+    const int t = off + i;
+    const int lb = min(t >> 4, p.max_blocks - 1);
+    const int phys = min(max(p.bt[(size_t)b * p.max_blocks + lb], 0), p.num_blocks - 1);
+    const size_t src = (size_t)(s0 + i) * p.cpt + piece;
+    const size_t dst = ((size_t)phys * 16 + (t & 15)) * p.cpt + piece;
+    p.k_pool[dst] = p.k_new[src];
+    p.v_pool[dst] = p.v_new[src];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+  AppendParams p;
+  p.k_new = (const uint4*)a.k_new;
+  p.v_new = (const uint4*)a.v_new;
+  p.cu = a.cu_new;
+  p.bt = a.block_table;
+  p.ctx = a.ctx_lens;
+  p.k_pool = (uint4*)a.k_pool;
+  p.v_pool = (uint4*)a.v_pool;
+  p.cpt = a.h_kv * a.head_dim / 8;
+  p.max_blocks = a.max_blocks_per_seq;
+  p.num_blocks = a.num_blocks;
+  p.max_ctx = a.max_ctx_len;
+  const dim3 grid((a.max_new + kTokPerWG - 1) / kTokPerWG, a.n_seqs);
+  hipLaunchKernelGGL(kv_append_kernel, grid, dim3(kAppendThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace cgqa

@@ -51,16 +51,27 @@ constexpr int kNTH = 64 * kQWaves;     // threads per work-group
 
 struct FwdParams {
   const f16* __restrict__ q;
-  const f16* __restrict__ k;
-  const f16* __restrict__ v;
+  const f16* __restrict__ k;  // packed keys, or the paged key pool
+  const f16* __restrict__ v;  // packed values, or the paged value pool
   const int32_t* __restrict__ cu;
   f16* __restrict__ o;
-  float* __restrict__ lse;
+  float* __restrict__ lse;    // may be null for the paged prefill
+  // Paged prefill only: block table [n_seqs, max_blocks], context lengths
+  // (new tokens included) and the pool size.
+  const int32_t* __restrict__ bt;
+  const int32_t* __restrict__ ctx;
+  int max_blocks, num_blocks, max_ctx;
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles;
   float scale_log2;  // scale * log2(e)
 };
 
-template <int D>
+// PAGED = false: the packed varlen forward (keys and values of sequence b
+// are rows cu[b] .. cu[b+1]-1 of k and v; query i sits at position i).
+// PAGED = true: the chunked prefill over a paged cache. The queries of
+// sequence b (rows cu[b] .. cu[b+1]-1 of q) are the last L_b of its ctx[b]
+// context positions, so query i sits at position ctx[b] - L_b + i; the keys
+// and values of position t are slot t % 16 of pool block bt[b][t / 16].
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
@@ -87,10 +98,17 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   const int g = rem % p.h_kv;
   const int b = rem / p.h_kv;
   const int s0 = p.cu[b];
-  const int L = p.cu[b + 1] - s0;
+  const int L = p.cu[b + 1] - s0;  // queries of the sequence
   const int q_wg0 = qt * BR;
   if (q_wg0 >= L) return;  // uniform over the work-group
-  const int n_kt = (min(L, q_wg0 + BR) + kBC - 1) / kBC;
+  // off: position of the sequence's first query; Lk: its number of keys.
+  int off = 0, Lk = L;
+  if constexpr (PAGED) {
+    Lk = min(p.ctx[b], p.max_ctx);  // a context past the table is clamped
+    if (Lk < L) return;  // invalid batch (a chunk longer than its context)
+    off = Lk - L;
+  }
+  const int n_kt = (off + min(L, q_wg0 + BR) + kBC - 1) / kBC;
 
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -101,8 +119,10 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   const int j16 = lane & 15;
   const int hig = chunk * p.hpw + wave / p.nqb;  // head within the group
   const int head = g * p.G + min(hig, p.G - 1);
-  const int q0 = q_wg0 + (wave % p.nqb) * 32;
-  const int qpos = q0 + l32;
+  const int q0 = q_wg0 + (wave % p.nqb) * 32;  // first query row of the wave
+  const int qpos = q0 + l32;                    // this lane's query row
+  const int q0a = off + q0;                     // their context positions
+  const int qposa = off + qpos;
   const bool wave_has_rows = q0 < L && hig < p.G;
   const bool qvalid = qpos < L && hig < p.G;
 
@@ -110,13 +130,25 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   // fills rows (wave * IPW + i) * RPI + lane / CH; lane l lands in chunk slot
   // l % CH of its row and fetches the global chunk that the swizzle maps
   // there. Keys past the sequence fetch its last row: their scores are
-  // masked and their weights are zero.
+  // masked and their weights are zero. In the paged case the RPI rows of one
+  // instruction lie in one 16-token block (RPI divides 16), so its physical
+  // block is one wave-uniform scalar load; out-of-range table entries are
+  // clamped into the pool, so no access leaves it.
   auto issue_tile = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int r = (wave * IPW + i) * RPI + lane / CH;
       const int slot = (lane % CH) * 8;
-      const size_t row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
+      size_t row;
+      if constexpr (PAGED) {
+        const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
+        const int lb = min(t0 >> 4, p.max_blocks - 1);
+        const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
+        const int t = min(kt * kBC + r, Lk - 1);
+        row = ((size_t)(phys * 16 + (t - (lb << 4))) * p.h_kv + g) * D;
+      } else {
+        row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
+      }
       f16* kdst = Ks[stage] + (wave * IPW + i) * 64 * 8;
       f16* vdst = Vs[stage] + (wave * IPW + i) * 64 * 8;
       dma16(p.k + row + swz<D>(r, slot), kdst);
@@ -167,7 +199,7 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     else wait_vm_barrier<0>();
     if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % kStages);
 
-    if (!wave_has_rows || kt * kBC > q0 + 31) return;  // fully masked for this wave
+    if (!wave_has_rows || kt * kBC > q0a + 31) return;  // fully masked for this wave
     const f16* Kb = Ks[stage];
     const f16* Vb = Vs[stage];
     // S^T for the two 32-key halves of the tile, as two interleaved chains.
@@ -201,13 +233,13 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Causal mask (diagonal tiles only) and the tile maximum of raw scores.
-    if (kt * kBC + kBC - 1 > q0) {
+    if (kt * kBC + kBC - 1 > q0a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kt * kBC + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key > qpos) s[kb][i] = -INFINITY;
+          if (key > qposa) s[kb][i] = -INFINITY;
         }
       }
     }
@@ -286,12 +318,16 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
       *(f16x4*)(orow + 32 * db + 8 * r4 + 4 * hi) = w;
     }
   }
-  if (hi == 0) p.lse[(size_t)head * p.T + s0 + qpos] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (hi == 0 && (!PAGED || p.lse != nullptr))
+    p.lse[(size_t)head * p.T + s0 + qpos] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+namespace {
+
+template <bool PAGED>
+hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   FwdParams p;
   p.q = (const f16*)a.q;
   p.k = (const f16*)a.k;
@@ -299,6 +335,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.cu = a.cu_seqlens;
   p.o = (f16*)a.o;
   p.lse = a.lse;
+  p.bt = a.block_table;
+  p.ctx = a.ctx_lens;
+  p.max_blocks = a.max_blocks_per_seq;
+  p.num_blocks = a.num_blocks;
+  p.max_ctx = a.max_ctx_len;
   p.n_seqs = a.n_seqs;
   p.T = a.total_tokens;
   p.h_q = a.h_q;
@@ -313,10 +354,20 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.scale_log2 = a.scale * kLog2e;
   const dim3 grid(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(kNTH), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<128, PAGED>), grid, dim3(kNTH), 0, stream, p);
   else
-    hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(kNTH), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<64, PAGED>), grid, dim3(kNTH), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  return launch_fwd_impl<false>(a, stream);
+}
+
+hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
+  return launch_fwd_impl<true>(a, stream);
 }
 
 }  // namespace cgqa

@@ -8,6 +8,10 @@
 
 namespace cgqa {
 
+// Forward and paged prefill. For the prefill, k and v are the paged pools,
+// cu_seqlens packs the new query tokens (total_tokens of them, at most
+// max_seqlen per sequence), ctx_lens holds each sequence's context length
+// (new tokens included) and lse may be null.
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -15,8 +19,23 @@ struct FwdArgs {
   const int32_t* cu_seqlens;
   void* o;
   float* lse;
+  const int32_t* block_table = nullptr;
+  const int32_t* ctx_lens = nullptr;
+  int max_blocks_per_seq = 0, num_blocks = 0, max_ctx_len = 0;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   float scale;
+};
+
+// New keys and values of a chunked prefill, written into the paged pools.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* cu_new;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  void* k_pool;
+  void* v_pool;
+  int n_seqs, max_new, h_kv, head_dim, max_blocks_per_seq, num_blocks, max_ctx_len;
 };
 
 struct BwdArgs {
@@ -76,6 +95,8 @@ inline QTileLayout qtile_layout(int G) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

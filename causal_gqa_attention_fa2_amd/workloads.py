@@ -21,6 +21,9 @@ Workloads (shapes of the RL.cu stack's Qwen3-0.6B attention; pitchhut
 * ``paged_decode``  256 sequences, ctx U{128..4096}, block 16, H_q=16,
   H_kv=8, d=128; the logical blocks of all sequences (in order) receive a
   seeded random permutation of the physical blocks.
+* ``paged_prefill`` one chunked-prefill step of a GRPO group: 32 sequences
+  with a cached context U{0..1536} and a new chunk U{128..512}, block 16,
+  H_q=16, H_kv=8, d=128; blocks permuted as for the decode.
 """
 import math
 
@@ -35,6 +38,10 @@ TRAIN_WORKLOADS = {
 DECODE_WORKLOADS = {
     "paged_decode": dict(n=256, ctx_lo=128, ctx_hi=4096, block_size=16,
                          h_q=16, h_kv=8, d=128, seed=1004),
+}
+PREFILL_WORKLOADS = {
+    "paged_prefill": dict(n=32, prior_lo=0, prior_hi=1536, new_lo=128, new_hi=512,
+                          block_size=16, h_q=16, h_kv=8, d=128, seed=1005),
 }
 BLOCK_SIZE = 16
 
@@ -142,6 +149,75 @@ def decode_workload_inputs(name="paged_decode"):
 def poison_unused(inp):
     """NaN into every pool slot no sequence uses (tail slots of last blocks,
     spare blocks). Returns a new dict with cloned pools."""
+    k_pool = inp["k_pool"].clone()
+    v_pool = inp["v_pool"].clone()
+    bs = inp["block_size"]
+    used = torch.zeros(k_pool.shape[0], bs, dtype=torch.bool)
+    for b in range(inp["n"]):
+        c = int(inp["ctx_lens"][b])
+        for lb in range(math.ceil(c / bs)):
+            phys = int(inp["block_table"][b, lb])
+            used[phys, :min(bs, c - lb * bs)] = True
+    k_pool[~used] = float("nan")
+    v_pool[~used] = float("nan")
+    out = dict(inp)
+    out.update(k_pool=k_pool, v_pool=v_pool)
+    return out
+
+
+def make_prefill_inputs(prior_lens, new_lens, h_q, h_kv, d, seed, block_size=BLOCK_SIZE,
+                        max_blocks=None, spare_blocks=0):
+    """A chunked prefill step: sequence b has ``prior_lens[b]`` cached tokens
+    and ``new_lens[b]`` new ones (ctx_lens = prior + new, the new tokens are
+    the last positions). Draw order: block permutation, then q, k_new, v_new
+    [total_q, heads, d] packed by cu_q, then the pools. The pools hold random
+    values everywhere, including the slots the new tokens will be appended
+    to (stale data the append must overwrite); table entries past a
+    sequence's last block hold -1.
+    """
+    g = _gen(seed)
+    prior = [int(c) for c in prior_lens]
+    new = [int(c) for c in new_lens]
+    ctx = [a + b for a, b in zip(prior, new)]
+    nblk = [math.ceil(c / block_size) for c in ctx]
+    used = sum(nblk)
+    num_blocks = used + int(spare_blocks)
+    if max_blocks is None:
+        max_blocks = max(1, max(nblk) if nblk else 1)
+    perm = torch.randperm(num_blocks, generator=g)[:used].to(torch.int32)
+    table = torch.full((len(ctx), max_blocks), -1, dtype=torch.int32)
+    pos = 0
+    for b, nb in enumerate(nblk):
+        table[b, :nb] = perm[pos:pos + nb]
+        pos += nb
+    cu_q = cu_from_lens(new)
+    Tq = int(cu_q[-1])
+    q = _randn_f16((Tq, h_q, d), g)
+    k_new = _randn_f16((Tq, h_kv, d), g)
+    v_new = _randn_f16((Tq, h_kv, d), g)
+    k_pool = _randn_f16((num_blocks, block_size, h_kv, d), g)
+    v_pool = _randn_f16((num_blocks, block_size, h_kv, d), g)
+    return dict(q=q, k_new=k_new, v_new=v_new, cu_q=cu_q, k_pool=k_pool, v_pool=v_pool,
+                block_table=table, ctx_lens=torch.tensor(ctx, dtype=torch.int32),
+                prior_lens=prior, new_lens=new, n=len(ctx), total_q=Tq,
+                max_q_len=max(new) if new else 0, max_ctx=max(ctx) if ctx else 0,
+                h_q=h_q, h_kv=h_kv, d=d, block_size=block_size, num_blocks=num_blocks,
+                max_blocks=max_blocks, scale=1.0 / math.sqrt(d))
+
+
+def prefill_workload_inputs(name="paged_prefill"):
+    w = PREFILL_WORKLOADS[name]
+    g = _gen(w["seed"])
+    prior = torch.randint(w["prior_lo"], w["prior_hi"] + 1, (w["n"],), generator=g).tolist()
+    new = torch.randint(w["new_lo"], w["new_hi"] + 1, (w["n"],), generator=g).tolist()
+    max_blocks = math.ceil((w["prior_hi"] + w["new_hi"]) / w["block_size"])
+    return make_prefill_inputs(prior, new, w["h_q"], w["h_kv"], w["d"], w["seed"] + 7919,
+                               block_size=w["block_size"], max_blocks=max_blocks)
+
+
+def poison_unused_prefill(inp):
+    """NaN into every pool slot outside all contexts (tail slots of last
+    blocks, spare blocks). Returns a new dict with cloned pools."""
     k_pool = inp["k_pool"].clone()
     v_pool = inp["v_pool"].clone()
     bs = inp["block_size"]

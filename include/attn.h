@@ -162,6 +162,61 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
                               const int32_t* ctx_lens, void* o, float scale, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Shape of a chunked prefill over a paged cache: `paged` describes the
+ * pools, the block table and the contexts (ctx_lens count each sequence's
+ * context INCLUDING its new tokens; max_ctx_len bounds them); the new tokens
+ * are packed by cu_q (int32 [n_seqs + 1], 0 = cu_q[0] <= ... = total_q) with
+ * at most max_q_len per sequence (host copies that size the launch). */
+typedef struct attn_prefill_dims {
+    attn_paged_dims paged;
+    int32_t total_q;
+    int32_t max_q_len;
+} attn_prefill_dims;
+
+/*
+ * attn_kv_append -- write the new keys and values of a chunked prefill into
+ * the paged pools (the rollout engine's paged key/value cache; pitchhut "Key
+ * Features" item 2).
+ *   k_new, v_new fp16 [total_q, h_kv, d]  new keys / values packed by cu_q
+ *   cu_q        int32 [n_seqs + 1]
+ *   block_table int32 [n_seqs, max_blocks_per_seq]
+ *   ctx_lens    int32 [n_seqs]   context lengths including the new tokens
+ *   k_pool, v_pool fp16 [num_blocks, 16, h_kv, d]  updated in place
+ * New token i of sequence b (L_b = cu_q[b+1] - cu_q[b] of them) is context
+ * position t = ctx_lens[b] - L_b + i and lands in slot t % 16 of block
+ * block_table[b][t / 16]. No other pool slot is written. A sequence whose
+ * L_b exceeds its context is skipped (invalid input; attn_check_prefill
+ * reports it). Table entries outside [0, num_blocks) and contexts above
+ * max_ctx_len are clamped, so no access leaves the pools (the result is then
+ * undefined). Each sequence's new positions must map to distinct slots.
+ */
+attn_status attn_kv_append(const attn_prefill_dims* dims, const void* k_new, const void* v_new,
+                           const int32_t* cu_q, const int32_t* block_table,
+                           const int32_t* ctx_lens, void* k_pool, void* v_pool, void* stream);
+
+/*
+ * attn_prefill_paged -- causal GQA attention of the new query tokens of a
+ * chunked prefill against each sequence's whole context in the paged pools
+ * (run after attn_kv_append has stored the chunk's keys and values).
+ *   q           fp16 [total_q, h_q, d]   new queries packed by cu_q
+ *   k_pool, v_pool fp16 [num_blocks, 16, h_kv, d]
+ *   block_table, ctx_lens, cu_q   as for attn_kv_append
+ *   o           fp16 [total_q, h_q, d]   output, fully overwritten
+ *   lse         fp32 [h_q, total_q] natural-log log-sum-exp per row, or
+ *               NULL when not needed
+ * New token i of sequence b sits at context position
+ * p = ctx_lens[b] - L_b + i and attends to positions 0..p (the same S, LSE
+ * and O as attn_fwd, whose causal mask is the case ctx_lens[b] = L_b).
+ * Positions past a sequence's context are never read. Rounding as attn_fwd;
+ * bitwise reproducible. A sequence whose L_b exceeds its context is skipped
+ * (its rows are left unwritten). Clamping of bad table entries and contexts
+ * as for attn_kv_append.
+ */
+attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* ctx_lens, const int32_t* cu_q, void* o,
+                               float* lse, float scale, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status status);
 
@@ -180,6 +235,13 @@ attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* c
  * entry in [0, num_blocks). Returns ATTN_OK or ATTN_ERR_INVALID_ARG. */
 attn_status attn_check_paged(const attn_paged_dims* dims, const int32_t* block_table_host,
                              const int32_t* ctx_lens_host);
+
+/* Host-side check of HOST copies of cu_q, block_table and ctx_lens against
+ * a prefill's dims: the attn_check_paged conditions, cu_q rising from 0 to
+ * total_q with every L_b <= max_q_len, and L_b <= ctx_lens[b]. Returns ATTN_OK
+ * or ATTN_ERR_INVALID_ARG. Makes no HIP call. */
+attn_status attn_check_prefill(const attn_prefill_dims* dims, const int32_t* cu_q_host,
+                               const int32_t* block_table_host, const int32_t* ctx_lens_host);
 
 #ifdef __cplusplus
 }

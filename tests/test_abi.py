@@ -169,3 +169,53 @@ def test_binding_rejects_host_tensors():
         A.fwd(q, k, k, cu)
     with pytest.raises(TypeError):
         A.fwd(q.float(), k, k, cu)
+
+
+def test_prefill_argument_checks(lib):
+    """attn_kv_append / attn_prefill_paged reject bad shapes and pointers
+    before any HIP call; an empty batch is a no-op."""
+    from causal_gqa_attention_fa2_amd.attn import PrefillDims
+    p = ctypes.c_void_p
+
+    def dims(n=4, h_q=16, h_kv=8, d=128, bs=16, maxb=64, nb=1000, max_ctx=1024, tq=300, mq=100):
+        return PrefillDims(PagedDims(n, h_q, h_kv, d, bs, maxb, nb, max_ctx), tq, mq)
+
+    def pre(dm, q=FAKE, cu=FAKE, lse=FAKE):
+        return lib.attn_prefill_paged(ctypes.byref(dm), p(q), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                      p(cu), p(FAKE), p(lse), 0.1, None)
+
+    def app(dm, kn=FAKE, bt=FAKE):
+        return lib.attn_kv_append(ctypes.byref(dm), p(kn), p(FAKE), p(FAKE), p(bt), p(FAKE),
+                                  p(FAKE), p(FAKE), None)
+
+    assert lib.attn_prefill_paged(None, *([p(FAKE)] * 8), 0.1, None) == INVALID
+    for fn in (pre, app):
+        assert fn(dims(bs=32)) == UNSUPPORTED
+        assert fn(dims(d=96)) == UNSUPPORTED
+        assert fn(dims(h_q=12)) == INVALID
+        assert fn(dims(maxb=10)) == INVALID           # table shorter than max_ctx
+        assert fn(dims(mq=301)) == INVALID            # longer than total_q
+        assert fn(dims(mq=2000, tq=3000)) == INVALID  # chunk longer than any context
+        assert fn(dims(mq=0)) == INVALID              # tokens but no chunk length
+        assert fn(dims(n=0, tq=0, mq=0)) == OK        # empty batch
+        assert fn(dims(tq=0, mq=0)) == OK             # no new tokens
+    assert pre(dims(), q=0) == INVALID
+    assert pre(dims(), cu=FAKE + 2) == INVALID
+    assert pre(dims(), lse=FAKE + 4) == INVALID
+    assert app(dims(), kn=0) == INVALID
+    assert app(dims(), bt=FAKE + 1) == INVALID
+
+
+def test_prefill_host_validator():
+    from causal_gqa_attention_fa2_amd.attn import PrefillDims
+    pd = PrefillDims(PagedDims(2, 4, 2, 64, 16, 3, 5, 40), 12, 10)
+    bt = torch.tensor([[4, 0, -1], [1, 2, 3]], dtype=torch.int32)
+    ctx = torch.tensor([17, 40], dtype=torch.int32)
+    chk = A.attn.check_prefill_host
+    assert chk(pd, torch.tensor([0, 2, 12]), bt, ctx) == OK
+    assert chk(pd, torch.tensor([0, 2, 11]), bt, ctx) == INVALID   # does not end at total_q
+    assert chk(pd, torch.tensor([0, 0, 12]), bt, ctx) == INVALID   # chunk above max_q_len
+    assert chk(pd, torch.tensor([1, 2, 12]), bt, ctx) == INVALID   # does not start at 0
+    small = torch.tensor([1, 40], dtype=torch.int32)
+    assert chk(pd, torch.tensor([0, 2, 12]), bt, small) == INVALID  # chunk longer than context
+    assert chk(pd, torch.tensor([0, 2, 12]), bt, torch.tensor([33, 40])) == INVALID  # entry -1
