@@ -12,7 +12,10 @@ pair for the forward, 2.5x that for the backward) from HIP events on the
 launch stream; the decode bandwidth (algorithmic bytes / event time) rides
 along in ``decode``. ``roofline`` reports the kernel that takes the most time
 per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same training workload.
+bounded sample of the same training workload. ``prefill`` times the rollout
+engine's chunked prefill (attn_kv_append + attn_prefill_paged on the
+paged_prefill workload) separately, after the timed steps; it is not part of
+``value``.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -125,6 +128,61 @@ def cpu_baseline(budget_s):
             "sample": f"{n} (sequence, KV-group) slices of {TRAIN_WORKLOAD} "
                       f"({len(slices)} per batch), fwd+bwd in fp64, {dt:.1f} s wall",
             "seconds": dt}
+
+
+PREFILL_WORKLOAD = "paged_prefill"
+
+
+def prefill_costs(inp):
+    """Causal FLOPs of a chunked prefill (query i of sequence b sees
+    prior_b + i + 1 positions) and the append's algorithmic bytes."""
+    d, h_q, h_kv = inp["d"], inp["h_q"], inp["h_kv"]
+    pairs = sum(L * p + L * (L + 1) // 2 for p, L in zip(inp["prior_lens"], inp["new_lens"]))
+    append_bytes = 2 * 2 * inp["total_q"] * h_kv * d * 2  # k and v, read and write
+    return 4 * d * h_q * pairs, append_bytes
+
+
+def bench_prefill(attn, W, dev, iters):
+    """The rollout engine's chunked prefill on the paged_prefill workload,
+    timed on its own (not part of `value`): attn_kv_append and
+    attn_prefill_paged, each averaged over back-to-back launches."""
+    import torch
+    inp = W.prefill_workload_inputs(PREFILL_WORKLOAD)
+    q, kn, vn, cu, kp, vp, bt, ctx = (inp[n].to(dev) for n in (
+        "q", "k_new", "v_new", "cu_q", "k_pool", "v_pool", "block_table", "ctx_lens"))
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=dev)
+    kw = dict(max_ctx_len=inp["max_ctx"], max_q_len=inp["max_q_len"])
+
+    def append():
+        attn.kv_append(kn, vn, cu, bt, ctx, kp, vp, **kw)
+
+    def prefill():
+        attn.prefill_paged(q, kp, vp, bt, ctx, cu, inp["scale"], o=o, lse=lse, **kw)
+
+    def timed(fn):
+        """Average time of `iters` back-to-back launches (HIP events on the
+        launch stream around the whole run)."""
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(iters):
+            fn()
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+
+    t_app = timed(append)  # rewrites the same slots: idempotent
+    t_att = timed(prefill)
+    flops, app_bytes = prefill_costs(inp)
+    return {"workload": "paged_prefill (32 seqs, cached U{0..1536} + new U{128..512}, "
+                        "block 16, H_q=16, H_kv=8, d=128)",
+            "append_us": round(t_app * 1e6, 2),
+            "append_GB/s": round(app_bytes / t_app / 1e9, 1),
+            "attn_us": round(t_att * 1e6, 2),
+            "attn_TFLOP/s": round(flops / t_att / 1e12, 2),
+            "attn_mfma_peak_frac": round(flops / t_att / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
 def main():
@@ -261,6 +319,7 @@ def main():
         "roofline": roofline,
         "source_digest": source_digest(),
     }
+    out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_budget)
         cb.pop("seconds", None)

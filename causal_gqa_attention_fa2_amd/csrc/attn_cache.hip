@@ -38,18 +38,23 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   const int i0 = blockIdx.x * kTokPerWG;
   if (i0 >= L || c < L) return;  // nothing here, or an invalid batch
   const int off = c - L;
-  const int n = min(kTokPerWG, L - i0) * p.cpt;
-  for (int e = threadIdx.x; e < n; e += kAppendThreads) {
-    const int tok = e / p.cpt;
-    const int piece = e - tok * p.cpt;
-    const int i = i0 + tok;
-    const int t = off + i;
+  const int ntok = min(kTokPerWG, L - i0);
+  // Pool row of each of the work-group's tokens, looked up once.
+  __shared__ size_t dst_row[kTokPerWG];
+  if (threadIdx.x < ntok) {
+    const int t = off + i0 + threadIdx.x;
     const int lb = min(t >> 4, p.max_blocks - 1);
     const int phys = min(max(p.bt[(size_t)b * p.max_blocks + lb], 0), p.num_blocks - 1);
-    const size_t src = (size_t)(s0 + i) * p.cpt + piece;
-    const size_t dst = ((size_t)phys * 16 + (t & 15)) * p.cpt + piece;
-    p.k_pool[dst] = p.k_new[src];
-    p.v_pool[dst] = p.v_new[src];
+    dst_row[threadIdx.x] = ((size_t)phys * 16 + (t & 15)) * p.cpt;
+  }
+  __syncthreads();
+  const int n = ntok * p.cpt;
+  const size_t src0 = (size_t)(s0 + i0) * p.cpt;  // the tokens' rows are contiguous
+  for (int e = threadIdx.x; e < n; e += kAppendThreads) {
+    const int tok = e / p.cpt;
+    const size_t dst = dst_row[tok] + (e - tok * p.cpt);
+    p.k_pool[dst] = p.k_new[src0 + e];
+    p.v_pool[dst] = p.v_new[src0 + e];
   }
 }
 
