@@ -219,3 +219,15 @@ def test_prefill_host_validator():
     small = torch.tensor([1, 40], dtype=torch.int32)
     assert chk(pd, torch.tensor([0, 2, 12]), bt, small) == INVALID  # chunk longer than context
     assert chk(pd, torch.tensor([0, 2, 12]), bt, torch.tensor([33, 40])) == INVALID  # entry -1
+
+
+def test_debug_validate_prefill_helper():
+    """The prefill check that ATTN_DEBUG_VALIDATE=1 runs raises on a chunk
+    longer than its context."""
+    from causal_gqa_attention_fa2_amd.attn import PrefillDims
+    pd = PrefillDims(PagedDims(2, 4, 2, 64, 16, 3, 5, 40), 12, 10)
+    bt = torch.tensor([[4, 0, -1], [1, 2, 3]], dtype=torch.int32)
+    cu = torch.tensor([0, 2, 12], dtype=torch.int32)
+    A.attn.validate_prefill(pd, cu, bt, torch.tensor([17, 40], dtype=torch.int32))
+    with pytest.raises(A.attn.AttnError):
+        A.attn.validate_prefill(pd, cu, bt, torch.tensor([1, 40], dtype=torch.int32))
