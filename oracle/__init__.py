@@ -21,6 +21,8 @@ of masked softmax attention, evaluated naively in float64:
 * ``kv_append_ref`` and ``attn_prefill_ref`` -- the rollout engine's chunked
   prefill: new tokens written into the paged pool, then causal attention of
   the new queries against the whole paged context.
+* ``rmsnorm_fwd_ref`` and ``rmsnorm_bwd_ref`` (module ``oracle.rmsnorm``) --
+  RMSNorm, the layer operation next to attention, and its backward.
 
 Every function is pinned by tests that do not re-use its formulas: closed
 forms, invariants, finite differences, a hand-derived worked example and
@@ -34,3 +36,4 @@ from .attention import (  # noqa: F401
     kv_append_ref,
     kv_head_of,
 )
+from .rmsnorm import rmsnorm_bwd_ref, rmsnorm_fwd_ref  # noqa: F401,E402
