@@ -35,8 +35,8 @@ MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense fp16
 HBM_PEAK_GBPS = 8000.0
 TRAIN_WORKLOAD = "qwen3_train"
 DECODE_WORKLOAD = "paged_decode"
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip", "cdna4.h",
-                  "kernels.h", "attn_api.cpp"]
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
+                  "attn_norm.hip", "cdna4.h", "kernels.h", "attn_api.cpp"]
 
 
 def causal_pairs(seqlens):

@@ -7,10 +7,13 @@ as hand-written HIP kernels behind the C ABI declared in include/attn.h.
 ``fwd``, ``bwd``, ``decode_paged``, ``kv_append`` and ``prefill_paged`` are
 thin ctypes wrappers of attn_fwd, attn_bwd, attn_decode_paged,
 attn_kv_append and attn_prefill_paged; the shared library is loaded on first
-use and every call raises if it is missing.
+use and every call raises if it is missing. ``rmsnorm_fwd`` / ``rmsnorm_bwd``
+wrap attn_rmsnorm_fwd / attn_rmsnorm_bwd, the layer normalisation next to
+attention.
 """
 from .attn import (  # noqa: F401
     AttnError,
+    NormDims,
     PagedDims,
     PrefillDims,
     VarlenDims,
@@ -24,5 +27,7 @@ from .attn import (  # noqa: F401
     paged_dims,
     prefill_dims,
     prefill_paged,
+    rmsnorm_bwd,
+    rmsnorm_fwd,
     varlen_dims,
 )

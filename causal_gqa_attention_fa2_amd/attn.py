@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTE
                 3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
+            "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
 
@@ -48,6 +49,10 @@ class PagedDims(ctypes.Structure):
 class PrefillDims(ctypes.Structure):
     _fields_ = [("paged", PagedDims), ("total_q", ctypes.c_int32),
                 ("max_q_len", ctypes.c_int32)]
+
+
+class NormDims(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("n", ctypes.c_int32)]
 
 
 _LIB = None
@@ -90,6 +95,14 @@ def load_library():
     lib.attn_prefill_paged.restype = ctypes.c_int
     lib.attn_check_prefill.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp]
     lib.attn_check_prefill.restype = ctypes.c_int
+    lib.attn_rmsnorm_fwd.argtypes = [ctypes.POINTER(NormDims), _vp, _vp, ctypes.c_float, _vp, _vp,
+                                     _vp]
+    lib.attn_rmsnorm_fwd.restype = ctypes.c_int
+    lib.attn_rmsnorm_bwd_workspace_bytes.argtypes = [ctypes.POINTER(NormDims)]
+    lib.attn_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_rmsnorm_bwd.argtypes = [ctypes.POINTER(NormDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]
+    lib.attn_rmsnorm_bwd.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -375,3 +388,49 @@ def check_prefill_host(dims, cu_host, block_table_host, ctx_host):
     cx = ctx_host.to(torch.int32).contiguous()
     return int(load_library().attn_check_prefill(ctypes.byref(dims), _vp(cu.data_ptr()),
                                                  _vp(bt.data_ptr()), _vp(cx.data_ptr())))
+
+
+def _norm_dims(x, w):
+    _need(x, "x", torch.float16, 2)
+    _need(w, "w", torch.float16, 1, x.device)
+    if w.shape[0] != x.shape[1]:
+        raise ValueError("w must have x.shape[1] entries")
+    return NormDims(x.shape[0], x.shape[1])
+
+
+def rmsnorm_fwd(x, w, eps=1e-6, y=None, rstd=None):
+    """attn_rmsnorm_fwd: returns (y fp16 [rows, n], rstd fp32 [rows])."""
+    lib = load_library()
+    dims = _norm_dims(x, w)
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _need(y, "y", torch.float16, 2, x.device)
+    _need(rstd, "rstd", torch.float32, 1, x.device)
+    if y.shape != x.shape or rstd.shape[0] != x.shape[0]:
+        raise ValueError("y / rstd shape mismatch")
+    _check("attn_rmsnorm_fwd", lib.attn_rmsnorm_fwd(ctypes.byref(dims), _ptr(x), _ptr(w),
+                                                    float(eps), _ptr(y), _ptr(rstd), _stream()))
+    return y, rstd
+
+
+def rmsnorm_bwd(x, w, rstd, dy, dx=None, dw=None, workspace=None):
+    """attn_rmsnorm_bwd: returns (dx fp16 [rows, n], dw fp32 [n])."""
+    lib = load_library()
+    dims = _norm_dims(x, w)
+    _need(rstd, "rstd", torch.float32, 1, x.device)
+    _need(dy, "dy", torch.float16, 2, x.device)
+    if dy.shape != x.shape or rstd.shape[0] != x.shape[0]:
+        raise ValueError("dy / rstd shape mismatch")
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty(x.shape[1], dtype=torch.float32, device=x.device) if dw is None else dw
+    _need(dx, "dx", torch.float16, 2, x.device)
+    _need(dw, "dw", torch.float32, 1, x.device)
+    need = int(lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1, x.device)
+    _check("attn_rmsnorm_bwd",
+           lib.attn_rmsnorm_bwd(ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(rstd), _ptr(dy),
+                                _ptr(dx), _ptr(dw), _ptr(workspace), workspace.numel(),
+                                _stream()))
+    return dx, dw

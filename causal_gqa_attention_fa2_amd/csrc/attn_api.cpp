@@ -108,6 +108,17 @@ attn_status check_prefill(const attn_prefill_dims* d, bool* empty) {
   return ATTN_OK;
 }
 
+attn_status check_norm(const attn_norm_dims* d, bool* empty) {
+  if (!d || d->rows < 0 || d->n <= 0) return ATTN_ERR_INVALID_ARG;
+  if (d->n % 8 != 0 || d->n > cgqa::kNormMaxCols) return ATTN_ERR_UNSUPPORTED;
+  *empty = d->rows == 0;
+  return ATTN_OK;
+}
+
+size_t norm_ws_bytes(const attn_norm_dims* d) {
+  return align_up((size_t)cgqa::rmsnorm_bwd_num_wgs(d->rows, d->n) * d->n * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,6 +331,60 @@ attn_status attn_check_prefill(const attn_prefill_dims* dims, const int32_t* cu,
     if (len < 0 || len > dims->max_q_len || len > ctx[b]) return ATTN_ERR_INVALID_ARG;
   }
   return ATTN_OK;
+}
+
+attn_status attn_rmsnorm_fwd(const attn_norm_dims* dims, const void* x, const void* w,
+                             float eps, void* y, float* rstd, void* stream) {
+  bool empty = false;
+  attn_status st = check_norm(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (!(eps >= 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (empty) return ATTN_OK;
+  if (!x || !w || !y || !rstd) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || ((uintptr_t)rstd & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::NormArgs a;
+  a.x = x;
+  a.w = w;
+  a.y = y;
+  a.rstd = rstd;
+  a.rows = dims->rows;
+  a.n = dims->n;
+  a.eps = eps;
+  return cgqa::launch_rmsnorm_fwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_rmsnorm_bwd_workspace_bytes(const attn_norm_dims* dims) {
+  bool empty = false;
+  if (check_norm(dims, &empty) != ATTN_OK || empty) return 0;
+  return norm_ws_bytes(dims);
+}
+
+attn_status attn_rmsnorm_bwd(const attn_norm_dims* dims, const void* x, const void* w,
+                             const float* rstd, const void* dy, void* dx, float* dw,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  attn_status st = check_norm(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!x || !w || !rstd || !dy || !dx || !dw) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dy) || !aligned16(dx) ||
+      ((uintptr_t)rstd & 3u) || ((uintptr_t)dw & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < norm_ws_bytes(dims) || ((uintptr_t)workspace % kWsAlign))
+    return ATTN_ERR_WORKSPACE;
+  cgqa::NormArgs a;
+  a.x = x;
+  a.w = w;
+  a.dy = dy;
+  a.dx = dx;
+  a.rstd = const_cast<float*>(rstd);
+  a.part = (float*)workspace;
+  a.dw = dw;
+  a.rows = dims->rows;
+  a.n = dims->n;
+  a.eps = 0.f;
+  return cgqa::launch_rmsnorm_bwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu) {

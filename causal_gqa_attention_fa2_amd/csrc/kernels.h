@@ -94,6 +94,27 @@ inline QTileLayout qtile_layout(int G) {
   return QTileLayout{hpw, kQWaves / hpw, (G + hpw - 1) / hpw};
 }
 
+// RMSNorm over rows of n fp16 values (n % 8 == 0, 8 <= n <= kNormMaxCols).
+// The backward writes one fp32 partial dw row per work-group (at most
+// kNormMaxWGs of them) into `part`, then sums them into dw.
+constexpr int kNormMaxCols = 2048;
+constexpr int kNormMaxWGs = 1024;
+struct NormArgs {
+  const void* x;
+  const void* w;
+  const void* dy = nullptr;
+  void* y = nullptr;
+  void* dx = nullptr;
+  float* rstd;
+  float* part = nullptr;
+  float* dw = nullptr;
+  int rows, n;
+  float eps;
+};
+int rmsnorm_bwd_num_wgs(int rows, int n);
+hipError_t launch_rmsnorm_fwd(const NormArgs& a, hipStream_t stream);
+hipError_t launch_rmsnorm_bwd(const NormArgs& a, hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

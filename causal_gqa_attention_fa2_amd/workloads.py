@@ -24,6 +24,9 @@ Workloads (shapes of the RL.cu stack's Qwen3-0.6B attention; pitchhut
 * ``paged_prefill`` one chunked-prefill step of a GRPO group: 32 sequences
   with a cached context U{0..1536} and a new chunk U{128..512}, block 16,
   H_q=16, H_kv=8, d=128; blocks permuted as for the decode.
+* ``qwen3_rmsnorm`` the layer RMSNorm of the training batch: 8192 rows
+  (B=8 x S=1024) of hidden size 1024; ``qwen3_qknorm`` the per-head
+  query norm: 8192 x 16 rows of 128. x, dy ~ N(0,1); w = 1 + 0.1 N(0,1).
 """
 import math
 
@@ -38,6 +41,10 @@ TRAIN_WORKLOADS = {
 DECODE_WORKLOADS = {
     "paged_decode": dict(n=256, ctx_lo=128, ctx_hi=4096, block_size=16,
                          h_q=16, h_kv=8, d=128, seed=1004),
+}
+NORM_WORKLOADS = {
+    "qwen3_rmsnorm": dict(rows=8192, n=1024, seed=1006),
+    "qwen3_qknorm": dict(rows=8192 * 16, n=128, seed=1007),
 }
 PREFILL_WORKLOADS = {
     "paged_prefill": dict(n=32, prior_lo=0, prior_hi=1536, new_lo=128, new_hi=512,
@@ -232,3 +239,18 @@ def poison_unused_prefill(inp):
     out = dict(inp)
     out.update(k_pool=k_pool, v_pool=v_pool)
     return out
+
+
+def make_norm_inputs(rows, n, seed):
+    """RMSNorm inputs: x [rows, n], dy [rows, n] ~ N(0,1) and a weight
+    w [n] = 1 + 0.1 N(0,1), all fp16 (draw order w, x, dy)."""
+    g = _gen(seed)
+    w = (1.0 + 0.1 * torch.randn(n, generator=g, dtype=torch.float32)).half()
+    x = _randn_f16((rows, n), g)
+    dy = _randn_f16((rows, n), g)
+    return dict(x=x, w=w, dy=dy, rows=rows, n=n, eps=1e-6)
+
+
+def norm_workload_inputs(name):
+    w = NORM_WORKLOADS[name]
+    return make_norm_inputs(w["rows"], w["n"], w["seed"])

@@ -217,6 +217,46 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
                                const int32_t* ctx_lens, const int32_t* cu_q, void* o,
                                float* lse, float scale, void* stream);
 
+/* Shape of an RMSNorm call: `rows` rows of `n` values (n % 8 == 0,
+ * 8 <= n <= 2048; rows >= 0). */
+typedef struct attn_norm_dims {
+    int32_t rows;
+    int32_t n;
+} attn_norm_dims;
+
+/*
+ * attn_rmsnorm_fwd -- RMSNorm, the layer operation next to attention in the
+ * Qwen3 stack (pitchhut "Project Highlights"):
+ *   r_i = 1 / sqrt(mean_j x_ij^2 + eps),  y_ij = x_ij r_i w_j.
+ *   x     fp16 [rows, n]    input rows
+ *   w     fp16 [n]          weight
+ *   y     fp16 [rows, n]    output, fully overwritten (may not alias x)
+ *   rstd  fp32 [rows]       r_i, fully overwritten (attn_rmsnorm_bwd needs it)
+ * fp32 sums; y rounded to nearest-even fp16.
+ */
+attn_status attn_rmsnorm_fwd(const attn_norm_dims* dims, const void* x, const void* w,
+                             float eps, void* y, float* rstd, void* stream);
+
+/* Bytes of device workspace attn_rmsnorm_bwd needs (fp32 partial dw rows,
+ * one per backward work-group; 0 for rows == 0). */
+size_t attn_rmsnorm_bwd_workspace_bytes(const attn_norm_dims* dims);
+
+/*
+ * attn_rmsnorm_bwd -- gradients of sum(y * dy) for attn_rmsnorm_fwd:
+ *   dx_ij = r_i (w_j dy_ij - xh_ij mean_k(w_k dy_ik xh_ik)),  xh = x r,
+ *   dw_j  = sum_i dy_ij xh_ij.
+ *   x, w   as given to attn_rmsnorm_fwd;  rstd fp32 [rows] its output
+ *   dy     fp16 [rows, n]
+ *   dx     fp16 [rows, n]   fully overwritten (may not alias x or dy)
+ *   dw     fp32 [n]         fully overwritten (not accumulated into)
+ *   workspace  at least attn_rmsnorm_bwd_workspace_bytes(dims) bytes,
+ *              256-byte aligned
+ * dw sums the rows in a fixed order: bitwise reproducible.
+ */
+attn_status attn_rmsnorm_bwd(const attn_norm_dims* dims, const void* x, const void* w,
+                             const float* rstd, const void* dy, void* dx, float* dw,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status status);
 

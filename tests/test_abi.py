@@ -231,3 +231,34 @@ def test_debug_validate_prefill_helper():
     A.attn.validate_prefill(pd, cu, bt, torch.tensor([17, 40], dtype=torch.int32))
     with pytest.raises(A.attn.AttnError):
         A.attn.validate_prefill(pd, cu, bt, torch.tensor([1, 40], dtype=torch.int32))
+
+
+def test_rmsnorm_argument_checks(lib):
+    from causal_gqa_attention_fa2_amd.attn import NormDims
+    p = ctypes.c_void_p
+
+    def fwd(d, x=FAKE, rstd=FAKE, eps=1e-6):
+        return lib.attn_rmsnorm_fwd(ctypes.byref(d), p(x), p(FAKE), eps, p(FAKE), p(rstd), None)
+
+    def bwd(d, ws=FAKE, nbytes=1 << 30, dw=FAKE):
+        return lib.attn_rmsnorm_bwd(ctypes.byref(d), p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                    p(dw), p(ws), nbytes, None)
+
+    assert fwd(NormDims(10, 100)) == UNSUPPORTED   # n % 8
+    assert fwd(NormDims(10, 4096)) == UNSUPPORTED  # n above 2048
+    assert fwd(NormDims(-1, 128)) == INVALID
+    assert fwd(NormDims(10, 0)) == INVALID
+    assert fwd(NormDims(10, 128), eps=-1.0) == INVALID
+    assert fwd(NormDims(10, 128), x=0) == INVALID
+    assert fwd(NormDims(10, 128), rstd=FAKE + 2) == INVALID
+    assert fwd(NormDims(0, 128), x=0) == OK        # no rows: nothing to do
+    need = lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(8192, 1024)))
+    assert need == min(8192 // 4, 1024) * 1024 * 4  # a partial row per 4 rows, at most 1024
+    assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(40, 1024))) == 10 * 4096
+    assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(1 << 20, 1024))) == \
+        1024 * 1024 * 4
+    assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(0, 1024))) == 0
+    assert bwd(NormDims(8192, 1024), ws=0) == WORKSPACE
+    assert bwd(NormDims(8192, 1024), nbytes=need - 4) == WORKSPACE
+    assert bwd(NormDims(8192, 1024), dw=FAKE + 2) == INVALID
+    assert bwd(NormDims(8192, 100)) == UNSUPPORTED
