@@ -15,7 +15,8 @@ per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
 bounded sample of the same training workload. ``prefill`` times the rollout
 engine's chunked prefill (attn_kv_append + attn_prefill_paged on the
 paged_prefill workload) separately, after the timed steps; it is not part of
-``value``.
+``value``. ``rmsnorm`` likewise times RMSNorm forward and backward on the
+training batch's layer norm and per-head query norm (HBM-bound, GB/s).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -185,6 +186,52 @@ def bench_prefill(attn, W, dev, iters):
             "attn_mfma_peak_frac": round(flops / t_att / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
+def norm_bytes(rows, n):
+    """Algorithmic HBM bytes of RMSNorm: forward reads x, w and writes y,
+    rstd; backward reads x, w, rstd, dy and writes dx, dw."""
+    fwd = 2 * rows * n * 2 + n * 2 + rows * 4
+    bwd = 3 * rows * n * 2 + n * 2 + rows * 4 + n * 4
+    return fwd, bwd
+
+
+def bench_rmsnorm(attn, W, dev, iters):
+    """RMSNorm forward and backward on the training batch's layer norm
+    (8192 x 1024) and per-head query norm (131072 x 128), each averaged over
+    back-to-back launches; HBM-bound, reported against 8 TB/s."""
+    import torch
+    out = {}
+    for name in ("qwen3_rmsnorm", "qwen3_qknorm"):
+        inp = W.norm_workload_inputs(name)
+        x, w, dy = (inp[n].to(dev) for n in ("x", "w", "dy"))
+        y = torch.empty_like(x)
+        rstd = torch.empty(x.shape[0], dtype=torch.float32, device=dev)
+        dx = torch.empty_like(x)
+        dw = torch.empty(x.shape[1], dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, attn.rmsnorm_bwd_workspace_bytes(x.shape[0], x.shape[1])),
+                         dtype=torch.uint8, device=dev)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(iters):
+                fn()
+            ev[1].record()
+            ev[1].synchronize()
+            return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+
+        t_f = timed(lambda: attn.rmsnorm_fwd(x, w, inp["eps"], y=y, rstd=rstd))
+        t_b = timed(lambda: attn.rmsnorm_bwd(x, w, rstd, dy, dx=dx, dw=dw, workspace=ws))
+        b_f, b_b = norm_bytes(*x.shape)
+        out[name] = {"rows": x.shape[0], "n": x.shape[1],
+                     "fwd_us": round(t_f * 1e6, 2), "fwd_GB/s": round(b_f / t_f / 1e9, 1),
+                     "bwd_us": round(t_b * 1e6, 2), "bwd_GB/s": round(b_b / t_b / 1e9, 1),
+                     "fwd_hbm_peak_frac": round(b_f / t_f / 1e9 / HBM_PEAK_GBPS, 4),
+                     "bwd_hbm_peak_frac": round(b_b / t_b / 1e9 / HBM_PEAK_GBPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +367,7 @@ def main():
         "source_digest": source_digest(),
     }
     out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
+    out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_budget)
         cb.pop("seconds", None)

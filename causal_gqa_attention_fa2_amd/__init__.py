@@ -28,6 +28,7 @@ from .attn import (  # noqa: F401
     prefill_dims,
     prefill_paged,
     rmsnorm_bwd,
+    rmsnorm_bwd_workspace_bytes,
     rmsnorm_fwd,
     varlen_dims,
 )

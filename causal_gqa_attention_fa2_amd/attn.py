@@ -413,6 +413,10 @@ def rmsnorm_fwd(x, w, eps=1e-6, y=None, rstd=None):
     return y, rstd
 
 
+def rmsnorm_bwd_workspace_bytes(rows, n):
+    return int(load_library().attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(rows, n))))
+
+
 def rmsnorm_bwd(x, w, rstd, dy, dx=None, dw=None, workspace=None):
     """attn_rmsnorm_bwd: returns (dx fp16 [rows, n], dw fp32 [n])."""
     lib = load_library()

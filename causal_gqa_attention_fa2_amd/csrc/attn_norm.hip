@@ -171,15 +171,29 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_bwd_kernel(NormParams p)
   for (int j = threadIdx.x; j < n; j += kNormThreads) prow[j] = red[j];
 }
 
-// dw_j = sum of the partial rows in work-group order.
+// dw_j = sum of the partial rows. A work-group owns 64 columns; its four
+// waves sum the partial rows g = wave, wave + 4, ... (independent loads, so
+// many are in flight), then wave 0 adds the four wave sums in wave order, so
+// the result does not depend on timing.
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_dw_kernel(const float* __restrict__ part,
                                                                   float* __restrict__ dw,
                                                                   int n, int n_rows) {
-  const int j = blockIdx.x * kNormThreads + threadIdx.x;
-  if (j >= n) return;
+  __shared__ float sums[kNormThreads];
+  const int wave = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
   float s = 0.f;
-  for (int g = 0; g < n_rows; ++g) s += part[(size_t)g * n + j];
-  dw[j] = s;
+  if (j < n) {
+#pragma unroll 8
+    for (int g = wave; g < n_rows; g += kNormThreads / 64) s += part[(size_t)g * n + j];
+  }
+  sums[threadIdx.x] = s;
+  __syncthreads();
+  if (wave == 0 && j < n) {
+    float t = sums[threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / 64; ++w) t += sums[threadIdx.x + 64 * w];
+    dw[j] = t;
+  }
 }
 
 int lanes_per_row(int n) {
@@ -251,8 +265,8 @@ hipError_t launch_rmsnorm_bwd(const NormArgs& a, hipStream_t stream) {
     default: e = launch_bwd_lpr<64>(p, n_wgs, stream); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rmsnorm_dw_kernel, dim3((a.n + kNormThreads - 1) / kNormThreads),
-                     dim3(kNormThreads), 0, stream, (const float*)a.part, a.dw, a.n, n_wgs);
+  hipLaunchKernelGGL(rmsnorm_dw_kernel, dim3((a.n + 63) / 64), dim3(kNormThreads), 0, stream,
+                     (const float*)a.part, a.dw, a.n, n_wgs);
   return hipGetLastError();
 }
 

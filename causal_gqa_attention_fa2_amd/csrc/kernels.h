@@ -98,7 +98,7 @@ inline QTileLayout qtile_layout(int G) {
 // The backward writes one fp32 partial dw row per work-group (at most
 // kNormMaxWGs of them) into `part`, then sums them into dw.
 constexpr int kNormMaxCols = 2048;
-constexpr int kNormMaxWGs = 1024;
+constexpr int kNormMaxWGs = 256;
 struct NormArgs {
   const void* x;
   const void* w;
