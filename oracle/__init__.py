@@ -23,6 +23,8 @@ of masked softmax attention, evaluated naively in float64:
   the new queries against the whole paged context.
 * ``rmsnorm_fwd_ref`` and ``rmsnorm_bwd_ref`` (module ``oracle.rmsnorm``) --
   RMSNorm, the layer operation next to attention, and its backward.
+* ``sample_ref`` (module ``oracle.sampling``) -- temperature / top-k / top-p
+  sampling over logits with a caller-supplied uniform.
 
 Every function is pinned by tests that do not re-use its formulas: closed
 forms, invariants, finite differences, a hand-derived worked example and
@@ -37,3 +39,4 @@ from .attention import (  # noqa: F401
     kv_head_of,
 )
 from .rmsnorm import rmsnorm_bwd_ref, rmsnorm_fwd_ref  # noqa: F401,E402
+from .sampling import sample_ref  # noqa: F401,E402
