@@ -37,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAIN_WORKLOAD = "qwen3_train"
 DECODE_WORKLOAD = "paged_decode"
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
-                  "attn_norm.hip", "cdna4.h", "kernels.h", "attn_api.cpp"]
+                  "attn_norm.hip", "attn_sample.hip", "cdna4.h", "kernels.h", "attn_api.cpp"]
 
 
 def causal_pairs(seqlens):

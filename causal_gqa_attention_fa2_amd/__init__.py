@@ -30,5 +30,6 @@ from .attn import (  # noqa: F401
     rmsnorm_bwd,
     rmsnorm_bwd_workspace_bytes,
     rmsnorm_fwd,
+    sample,
     varlen_dims,
 )

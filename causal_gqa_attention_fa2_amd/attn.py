@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTE
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
             "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
+            "attn_sample",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
 
@@ -49,6 +50,10 @@ class PagedDims(ctypes.Structure):
 class PrefillDims(ctypes.Structure):
     _fields_ = [("paged", PagedDims), ("total_q", ctypes.c_int32),
                 ("max_q_len", ctypes.c_int32)]
+
+
+class SampleDims(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("vocab", ctypes.c_int32)]
 
 
 class NormDims(ctypes.Structure):
@@ -103,6 +108,9 @@ def load_library():
     lib.attn_rmsnorm_bwd.argtypes = [ctypes.POINTER(NormDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]
     lib.attn_rmsnorm_bwd.restype = ctypes.c_int
+    lib.attn_sample.argtypes = [ctypes.POINTER(SampleDims), _vp, _vp, ctypes.c_float,
+                                ctypes.c_int32, ctypes.c_float, _vp, _vp]
+    lib.attn_sample.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -438,3 +446,20 @@ def rmsnorm_bwd(x, w, rstd, dy, dx=None, dw=None, workspace=None):
                                 _ptr(dx), _ptr(dw), _ptr(workspace), workspace.numel(),
                                 _stream()))
     return dx, dw
+
+
+def sample(logits, u, temperature=1.0, top_k=50, top_p=1.0, tokens=None):
+    """attn_sample: returns tokens int32 [n_rows] (u: fp32 uniforms, one per row)."""
+    lib = load_library()
+    _need(logits, "logits", torch.float32, 2)
+    _need(u, "u", torch.float32, 1, logits.device)
+    if u.shape[0] != logits.shape[0]:
+        raise ValueError("u must have one entry per row")
+    tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=logits.device) \
+        if tokens is None else tokens
+    _need(tokens, "tokens", torch.int32, 1, logits.device)
+    dims = SampleDims(logits.shape[0], logits.shape[1])
+    _check("attn_sample", lib.attn_sample(ctypes.byref(dims), _ptr(logits), _ptr(u),
+                                          float(temperature), int(top_k), float(top_p),
+                                          _ptr(tokens), _stream()))
+    return tokens

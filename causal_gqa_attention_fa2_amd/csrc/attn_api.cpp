@@ -387,6 +387,30 @@ attn_status attn_rmsnorm_bwd(const attn_norm_dims* dims, const void* x, const vo
   return cgqa::launch_rmsnorm_bwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_sample(const attn_sample_dims* dims, const float* logits, const float* u,
+                        float temperature, int32_t top_k, float top_p, int32_t* tokens,
+                        void* stream) {
+  if (!dims || dims->n_rows < 0 || dims->vocab < 1) return ATTN_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || temperature > 3.0e38f) return ATTN_ERR_INVALID_ARG;
+  if (!(top_p > 0.f && top_p <= 1.f)) return ATTN_ERR_INVALID_ARG;
+  if (top_k < 1) return ATTN_ERR_INVALID_ARG;
+  if (top_k > cgqa::kMaxTopK) return ATTN_ERR_UNSUPPORTED;
+  if (dims->n_rows == 0) return ATTN_OK;
+  if (!logits || !u || !tokens) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)logits & 3u) || ((uintptr_t)u & 3u) || ((uintptr_t)tokens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::SampleArgs a;
+  a.logits = logits;
+  a.u = u;
+  a.tokens = tokens;
+  a.n_rows = dims->n_rows;
+  a.vocab = dims->vocab;
+  a.top_k = top_k;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  return cgqa::launch_sample(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_check_cu_seqlens(const attn_varlen_dims* dims, const int32_t* cu) {
   if (!dims || !cu || dims->n_seqs < 0) return ATTN_ERR_INVALID_ARG;
   if (cu[0] != 0) return ATTN_ERR_INVALID_ARG;

@@ -1,0 +1,219 @@
+// attn_sample.hip -- temperature / top-k / top-p sampling over logits for
+// gfx950, the rollout engine's step after the decode and the LM head
+// (pitchhut "Key Features", item 1).
+//
+// One work-group of 1024 threads per row:
+//  1. radix select (11 + 11 + 10 bits of an order-preserving key of the fp32
+//     logit, one LDS histogram per pass) finds K*, the k-th largest key;
+//  2. the keys above K* are gathered, then the lowest-index keys equal to K*
+//     until k are held (tiles of 1024 in index order, ranks from wave
+//     ballots), so the kept set is the first k of the ranking "logit
+//     descending, index ascending";
+//  3. a bitonic sort in LDS puts the k candidates in ranking order;
+//  4. weights w_j = exp((v_j - v_0) / T); one thread forms the cumulative
+//     sums c_j in ranking order, keeps ranks 0..cut with
+//     cut = min{j : c_j >= top_p c_last}, and returns the token at rank
+//     min{j <= cut : c_j > u c_cut} for the row's uniform u.
+// Scaling by 1/T > 0 keeps the order, so the selection runs on raw logits.
+// The result is a deterministic function of the logits and u.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace cgqa {
+namespace {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kWaves = kSampleThreads / 64;
+
+struct SampleParams {
+  const float* __restrict__ logits;
+  const float* __restrict__ u;
+  int32_t* __restrict__ tokens;
+  int vocab, k;
+  float inv_t, top_p;
+};
+
+// Larger float -> larger key (sign flipped for positives, all bits for
+// negatives); -inf maps below every finite value.
+__device__ __forceinline__ uint32_t fkey(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Ranking order: a before b when its logit is larger, or equal with a
+// smaller index.
+__device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t suf[kSampleThreads];
+  __shared__ float cval[kMaxTopK];
+  __shared__ int cidx[kMaxTopK];
+  __shared__ float cum[kMaxTopK];
+  __shared__ uint32_t s_digit, s_above, s_count, s_taken, s_wave[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int V = p.vocab;
+  const float* row = p.logits + (size_t)blockIdx.x * V;
+
+  // 1. Radix select of the k-th largest key: digits of 11, 11 and 10 bits
+  // from the top; `need` is the rank of K* among the keys matching the
+  // digits chosen so far.
+  uint32_t prefix = 0, need = (uint32_t)p.k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int bits = pass == 2 ? 10 : 11;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + bits));
+    hist[2 * tid] = 0;
+    hist[2 * tid + 1] = 0;
+    __syncthreads();
+    for (int i = tid; i < V; i += kSampleThreads) {
+      const uint32_t key = fkey(row[i]);
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
+    }
+    __syncthreads();
+    // Suffix sums over digit pairs (2t, 2t + 1), then the pair and digit
+    // where the count of larger digits first reaches `need`.
+    suf[tid] = hist[2 * tid] + hist[2 * tid + 1];
+    __syncthreads();
+    for (int off = 1; off < kSampleThreads; off <<= 1) {
+      const uint32_t add = tid + off < kSampleThreads ? suf[tid + off] : 0u;
+      __syncthreads();
+      suf[tid] += add;
+      __syncthreads();
+    }
+    const uint32_t above_pair = tid + 1 < kSampleThreads ? suf[tid + 1] : 0u;
+    if (suf[tid] >= need && above_pair < need) {
+      const uint32_t h1 = hist[2 * tid + 1];
+      if (above_pair + h1 >= need) {
+        s_digit = 2 * tid + 1;
+        s_above = above_pair;
+      } else {
+        s_digit = 2 * tid;
+        s_above = above_pair + h1;
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    need -= s_above;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;
+  const int n_gt = p.k - (int)need;  // keys above K*; `need` ties are taken
+
+  // 2. Gather: every key above K* (any slot order: the sort fixes it), then
+  // the `need` lowest-index keys equal to K*.
+  if (tid == 0) {
+    s_count = 0;
+    s_taken = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < V; i += kSampleThreads) {
+    const float v = row[i];
+    if (fkey(v) > kstar) {
+      const uint32_t slot = atomicAdd(&s_count, 1u);
+      cval[slot] = v;
+      cidx[slot] = i;
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < V; base += kSampleThreads) {
+    const uint32_t taken = s_taken;
+    if (taken >= need) break;  // uniform: read after the barrier below
+    const int i = base + tid;
+    const float v = i < V ? row[i] : 0.f;
+    const bool eq = i < V && fkey(v) == kstar;
+    const uint64_t ball = __ballot(eq);
+    if (lane == 0) s_wave[wave] = (uint32_t)__popcll(ball);
+    __syncthreads();
+    uint32_t rank = taken;
+    for (int w = 0; w < wave; ++w) rank += s_wave[w];
+    rank += (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+    if (eq && rank < need) {
+      cval[n_gt + rank] = v;
+      cidx[n_gt + rank] = i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kWaves; ++w) tot += s_wave[w];
+      s_taken = taken + tot;
+    }
+    __syncthreads();
+  }
+  // Unused slots sort last.
+  if (tid >= p.k) {
+    cval[tid] = -INFINITY;
+    cidx[tid] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+
+  // 3. Bitonic sort of the 1024 slots into ranking order.
+  for (int size = 2; size <= kSampleThreads; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int partner = tid ^ stride;
+      if (partner > tid) {
+        const float va = cval[tid], vb = cval[partner];
+        const int ia = cidx[tid], ib = cidx[partner];
+        const bool up = (tid & size) == 0;
+        if (up != before(va, ia, vb, ib)) {
+          cval[tid] = vb;
+          cidx[tid] = ib;
+          cval[partner] = va;
+          cidx[partner] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 4. Weights, then the cumulative sums and the draw in ranking order.
+  if (tid < p.k) cum[tid] = expf((cval[tid] - cval[0]) * p.inv_t);
+  __syncthreads();
+  if (tid == 0) {
+    float c = 0.f;
+    for (int j = 0; j < p.k; ++j) {
+      c += cum[j];
+      cum[j] = c;
+    }
+    const float thr = p.top_p * c;
+    int cut = p.k - 1;
+    for (int j = 0; j < p.k; ++j) {
+      if (cum[j] >= thr) {
+        cut = j;
+        break;
+      }
+    }
+    const float target = p.u[blockIdx.x] * cum[cut];
+    int pick = cut;
+    for (int j = 0; j <= cut; ++j) {
+      if (cum[j] > target) {
+        pick = j;
+        break;
+      }
+    }
+    p.tokens[blockIdx.x] = cidx[pick];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
+  SampleParams p;
+  p.logits = a.logits;
+  p.u = a.u;
+  p.tokens = a.tokens;
+  p.vocab = a.vocab;
+  p.k = a.top_k < a.vocab ? a.top_k : a.vocab;
+  p.inv_t = 1.f / a.temperature;
+  p.top_p = a.top_p;
+  hipLaunchKernelGGL(sample_kernel, dim3(a.n_rows), dim3(kSampleThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace cgqa

@@ -115,6 +115,17 @@ int rmsnorm_bwd_num_wgs(int rows, int n);
 hipError_t launch_rmsnorm_fwd(const NormArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm_bwd(const NormArgs& a, hipStream_t stream);
 
+// Sampling over logits: one work-group of kMaxTopK threads per row.
+constexpr int kMaxTopK = 1024;
+struct SampleArgs {
+  const float* logits;  // [n_rows, vocab]
+  const float* u;       // [n_rows] uniforms in [0, 1)
+  int32_t* tokens;      // [n_rows]
+  int n_rows, vocab, top_k;
+  float temperature, top_p;
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

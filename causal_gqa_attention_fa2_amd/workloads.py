@@ -24,6 +24,8 @@ Workloads (shapes of the RL.cu stack's Qwen3-0.6B attention; pitchhut
 * ``paged_prefill`` one chunked-prefill step of a GRPO group: 32 sequences
   with a cached context U{0..1536} and a new chunk U{128..512}, block 16,
   H_q=16, H_kv=8, d=128; blocks permuted as for the decode.
+* ``rollout_sampling`` 256 rows of Qwen3's 151936-token vocabulary, logits
+  3 N(0,1), temperature 0.6, top-k 20, top-p 0.95, one uniform per row.
 * ``qwen3_rmsnorm`` the layer RMSNorm of the training batch: 8192 rows
   (B=8 x S=1024) of hidden size 1024; ``qwen3_qknorm`` the per-head
   query norm: 8192 x 16 rows of 128. x, dy ~ N(0,1); w = 1 + 0.1 N(0,1).
@@ -41,6 +43,10 @@ TRAIN_WORKLOADS = {
 DECODE_WORKLOADS = {
     "paged_decode": dict(n=256, ctx_lo=128, ctx_hi=4096, block_size=16,
                          h_q=16, h_kv=8, d=128, seed=1004),
+}
+SAMPLE_WORKLOADS = {
+    "rollout_sampling": dict(n=256, vocab=151936, scale=3.0, temperature=0.6, top_k=20,
+                             top_p=0.95, seed=1008),
 }
 NORM_WORKLOADS = {
     "qwen3_rmsnorm": dict(rows=8192, n=1024, seed=1006),
@@ -254,3 +260,27 @@ def make_norm_inputs(rows, n, seed):
 def norm_workload_inputs(name):
     w = NORM_WORKLOADS[name]
     return make_norm_inputs(w["rows"], w["n"], w["seed"])
+
+
+def make_sample_inputs(n, vocab, scale, seed, step=None, masked=0.0):
+    """Logits [n, vocab] = scale N(0,1) in fp32 (rounded to multiples of
+    `step` when given, which creates ties; a `masked` fraction set to -inf,
+    never the first entry of a row) and uniforms u [n] in [0, 1). Draw
+    order: logits, mask, u."""
+    g = _gen(seed)
+    logits = torch.randn(n, vocab, generator=g, dtype=torch.float32) * scale
+    if step:
+        logits = torch.round(logits / step) * step
+    if masked > 0:
+        m = torch.rand(n, vocab, generator=g) < masked
+        m[:, 0] = False
+        logits[m] = float("-inf")
+    u = torch.rand(n, generator=g, dtype=torch.float32)
+    return dict(logits=logits, u=u, n=n, vocab=vocab)
+
+
+def sample_workload_inputs(name="rollout_sampling"):
+    w = SAMPLE_WORKLOADS[name]
+    inp = make_sample_inputs(w["n"], w["vocab"], w["scale"], w["seed"])
+    inp.update(temperature=w["temperature"], top_k=w["top_k"], top_p=w["top_p"])
+    return inp

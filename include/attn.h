@@ -257,6 +257,33 @@ attn_status attn_rmsnorm_bwd(const attn_norm_dims* dims, const void* x, const vo
                              const float* rstd, const void* dy, void* dx, float* dw,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Shape of a sampling call: n_rows rows of `vocab` logits. */
+typedef struct attn_sample_dims {
+    int32_t n_rows;
+    int32_t vocab;
+} attn_sample_dims;
+
+/*
+ * attn_sample -- temperature / top-k / top-p sampling, the rollout engine's
+ * step after the LM head (pitchhut "Key Features", item 1), with the random
+ * number supplied by the caller (one uniform per row), so the token is a
+ * deterministic function of the logits and u:
+ *   z = logits / temperature; rank tokens by z descending, ties by index
+ *   ascending; keep the first k = min(top_k, vocab); weights
+ *   w_j = exp(z_j - z_0) over the kept ranking with cumulative sums c_j;
+ *   cut = min{j : c_j >= top_p * c_(k-1)};
+ *   token = the one at rank min{j <= cut : c_j > u * c_cut}.
+ *   logits fp32 [n_rows, vocab]  finite or -inf, at least one finite per row
+ *   u      fp32 [n_rows]         uniforms in [0, 1)
+ *   tokens int32 [n_rows]        output
+ * Requires temperature > 0 (finite), 1 <= top_k <= 1024, 0 < top_p <= 1.
+ * fp32 arithmetic; a u within fp32 rounding of a cumulative boundary may
+ * pick the neighbouring rank.
+ */
+attn_status attn_sample(const attn_sample_dims* dims, const float* logits, const float* u,
+                        float temperature, int32_t top_k, float top_p, int32_t* tokens,
+                        void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status status);
 

@@ -262,3 +262,25 @@ def test_rmsnorm_argument_checks(lib):
     assert bwd(NormDims(8192, 1024), nbytes=need - 4) == WORKSPACE
     assert bwd(NormDims(8192, 1024), dw=FAKE + 2) == INVALID
     assert bwd(NormDims(8192, 100)) == UNSUPPORTED
+
+
+def test_sample_argument_checks(lib):
+    from causal_gqa_attention_fa2_amd.attn import SampleDims
+    p = ctypes.c_void_p
+
+    def call(d, t=0.7, k=20, tp=0.9, lg=FAKE, u=FAKE, out=FAKE):
+        return lib.attn_sample(ctypes.byref(d), p(lg), p(u), t, k, tp, p(out), None)
+
+    d = SampleDims(4, 1000)
+    assert call(SampleDims(-1, 1000)) == INVALID
+    assert call(SampleDims(4, 0)) == INVALID
+    assert call(d, t=0.0) == INVALID
+    assert call(d, t=float("nan")) == INVALID
+    assert call(d, t=float("inf")) == INVALID
+    assert call(d, k=0) == INVALID
+    assert call(d, k=1025) == UNSUPPORTED
+    assert call(d, tp=0.0) == INVALID
+    assert call(d, tp=1.5) == INVALID
+    assert call(d, lg=0) == INVALID
+    assert call(d, out=FAKE + 2) == INVALID
+    assert call(SampleDims(0, 1000), lg=0, u=0, out=0) == OK

@@ -1,0 +1,73 @@
+"""GPU parity of attn_sample (through the C ABI) against the fp64 oracle.
+
+The token is an integer decided by floating point: the kernel sums weights in
+fp32, the oracle in fp64. Where the oracle's cumulative sums leave a margin
+of more than 1e-5 (relative) around both decisions (the top-p cut and the
+draw), the tokens must be equal; inside that margin the kernel may pick the
+neighbouring rank, and the test checks that it did no worse than that.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity import W, attn
+from oracle import sample_ref
+from oracle.sampling import ranking
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-5
+
+# (rows, vocab, top_k, top_p, temperature, logit scale, tie step, masked fraction)
+CASES = [
+    (8, 1, 20, 0.9, 1.0, 1.0, None, 0.0),
+    (16, 7, 5, 1.0, 0.7, 2.0, None, 0.0),
+    (32, 1000, 50, 0.95, 0.6, 3.0, None, 0.0),
+    (32, 1024, 1024, 1.0, 1.0, 1.0, None, 0.0),
+    (32, 1025, 1024, 0.5, 1.3, 1.0, None, 0.0),
+    (32, 5000, 1, 0.9, 0.6, 3.0, None, 0.0),
+    (64, 3000, 64, 0.9, 1.0, 2.0, 0.5, 0.0),     # many exact ties, also at the k-th value
+    (32, 4096, 100, 1.0, 0.8, 2.0, None, 0.99),  # mostly -inf: fewer finite logits than k
+    (16, 151936, 20, 0.95, 0.6, 3.0, None, 0.0),
+]
+
+
+def _check(name, logits, u, T, k, tp, got):
+    lg = logits.numpy().astype(np.float64)
+    tok, cut, cum = sample_ref(lg, u.numpy(), T, k, tp)
+    got = got.cpu().numpy().astype(np.int64)
+    exact = near = 0
+    for b in range(lg.shape[0]):
+        c = cum[b]
+        m_cut = np.abs(c - tp * c[-1]).min() / c[-1]
+        m_pick = np.abs(c[:cut[b] + 1] - float(u[b]) * c[cut[b]]).min() / c[cut[b]]
+        if got[b] == tok[b]:
+            exact += 1
+            continue
+        assert min(m_cut, m_pick) <= MARGIN, (name, b, int(got[b]), int(tok[b]))
+        order = ranking(lg[b] / T)[:min(k, lg.shape[1])]
+        r_ref = int(np.nonzero(order == tok[b])[0][0])
+        r_got = np.nonzero(order == got[b])[0]
+        assert r_got.size and abs(int(r_got[0]) - r_ref) <= 1, (name, b)
+        near += 1
+    print(f"{name}: {exact} exact, {near} at a rounding boundary", flush=True)
+
+
+@pytest.mark.parametrize("n,V,k,tp,T,scale,step,masked", CASES, ids=lambda x: str(x))
+def test_sample_cases(gpu, n, V, k, tp, T, scale, step, masked):
+    inp = W.make_sample_inputs(n, V, scale, seed=7000 + V + k, step=step, masked=masked)
+    got = attn.sample(inp["logits"].to(gpu), inp["u"].to(gpu), T, k, tp)
+    torch.cuda.synchronize()
+    _check(f"sample n{n} V{V} k{k} p{tp} T{T}", inp["logits"], inp["u"], T, k, tp, got)
+
+
+def test_sample_workload(gpu):
+    inp = W.sample_workload_inputs("rollout_sampling")
+    lg, u = inp["logits"].to(gpu), inp["u"].to(gpu)
+    got = attn.sample(lg, u, inp["temperature"], inp["top_k"], inp["top_p"])
+    again = attn.sample(lg, u, inp["temperature"], inp["top_k"], inp["top_p"])
+    torch.cuda.synchronize()
+    assert torch.equal(got, again)  # deterministic
+    rows = slice(0, 64)
+    _check("rollout_sampling (64 rows)", inp["logits"][rows], inp["u"][rows],
+           inp["temperature"], inp["top_k"], inp["top_p"], got[rows])
