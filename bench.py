@@ -16,7 +16,8 @@ bounded sample of the same training workload. ``prefill`` times the rollout
 engine's chunked prefill (attn_kv_append + attn_prefill_paged on the
 paged_prefill workload) separately, after the timed steps; it is not part of
 ``value``. ``rmsnorm`` likewise times RMSNorm forward and backward on the
-training batch's layer norm and per-head query norm (HBM-bound, GB/s).
+training batch's layer norm and per-head query norm (HBM-bound, GB/s), and
+``sampling`` the rollout batch's temperature / top-k / top-p sampling.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -232,6 +233,35 @@ def bench_rmsnorm(attn, W, dev, iters):
     return out
 
 
+def bench_sampling(attn, W, dev, iters):
+    """Temperature / top-k / top-p sampling of the rollout batch (256 rows of
+    the 151936-token vocabulary), averaged over back-to-back launches. The
+    algorithmic bytes are one read of the logits (plus u and the tokens); the
+    kernel reads each row several times (radix passes), mostly from cache."""
+    import torch
+    inp = W.sample_workload_inputs("rollout_sampling")
+    lg, u = inp["logits"].to(dev), inp["u"].to(dev)
+    tok = torch.empty(lg.shape[0], dtype=torch.int32, device=dev)
+
+    def run():
+        attn.sample(lg, u, inp["temperature"], inp["top_k"], inp["top_p"], tokens=tok)
+
+    for _ in range(3):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(iters):
+        run()
+    ev[1].record()
+    ev[1].synchronize()
+    t = ev[0].elapsed_time(ev[1]) / iters * 1e-3
+    nbytes = lg.numel() * 4 + lg.shape[0] * 8
+    return {"workload": "rollout_sampling (256 x 151936 fp32 logits, T 0.6, top-k 20, "
+                        "top-p 0.95)",
+            "us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+            "hbm_peak_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +398,7 @@ def main():
     }
     out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
     out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
+    out["sampling"] = bench_sampling(attn, W, dev, max(args.steps, 5))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_budget)
         cb.pop("seconds", None)

@@ -5,10 +5,11 @@
 // One work-group of 1024 threads per row:
 //  1. radix select (11 + 11 + 10 bits of an order-preserving key of the fp32
 //     logit, one LDS histogram per pass) finds K*, the k-th largest key;
-//  2. the keys above K* are gathered, then the lowest-index keys equal to K*
-//     until k are held (tiles of 1024 in index order, ranks from wave
+//  2. the keys above K* are gathered (with the keys equal to K* when all of
+//     them are kept, the usual case; otherwise the lowest-index keys equal
+//     to K* follow, in tiles of 1024 in index order with ranks from wave
 //     ballots), so the kept set is the first k of the ranking "logit
-//     descending, index ascending";
+//     descending, index ascending"; the row is streamed with 16-byte loads;
 //  3. a bitonic sort in LDS puts the k candidates in ranking order;
 //  4. weights w_j = exp((v_j - v_0) / T); one thread forms the cumulative
 //     sums c_j in ranking order, keeps ranks 0..cut with
@@ -47,13 +48,45 @@ __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Calls fn(value, index) for every logit of the row: 16-byte loads, four in
+// flight per thread, when the row is 16-byte aligned; the rest one by one.
+template <typename F>
+__device__ __forceinline__ void for_each_logit(const float* row, int V, int tid, F&& fn) {
+  int done = 0;
+  if (((uintptr_t)row & 15u) == 0) {
+    const int v4 = V >> 2;
+    const float4* r4 = (const float4*)row;
+    constexpr int kU = 4;
+    for (int i0 = tid; i0 < v4; i0 += kU * kSampleThreads) {
+      float4 x[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int i = i0 + k * kSampleThreads;
+        if (i < v4) x[k] = r4[i];
+      }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int i = i0 + k * kSampleThreads;
+        if (i < v4) {
+          fn(x[k].x, 4 * i);
+          fn(x[k].y, 4 * i + 1);
+          fn(x[k].z, 4 * i + 2);
+          fn(x[k].w, 4 * i + 3);
+        }
+      }
+    }
+    done = v4 << 2;
+  }
+  for (int i = done + tid; i < V; i += kSampleThreads) fn(row[i], i);
+}
+
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t suf[kSampleThreads];
   __shared__ float cval[kMaxTopK];
   __shared__ int cidx[kMaxTopK];
   __shared__ float cum[kMaxTopK];
-  __shared__ uint32_t s_digit, s_above, s_count, s_taken, s_wave[kWaves];
+  __shared__ uint32_t s_digit, s_above, s_eq, s_count, s_taken, s_wave[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -72,10 +105,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     hist[2 * tid] = 0;
     hist[2 * tid + 1] = 0;
     __syncthreads();
-    for (int i = tid; i < V; i += kSampleThreads) {
-      const uint32_t key = fkey(row[i]);
+    for_each_logit(row, V, tid, [&](float x, int) {
+      const uint32_t key = fkey(x);
       if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
-    }
+    });
     __syncthreads();
     // Suffix sums over digit pairs (2t, 2t + 1), then the pair and digit
     // where the count of larger digits first reaches `need`.
@@ -93,9 +126,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
       if (above_pair + h1 >= need) {
         s_digit = 2 * tid + 1;
         s_above = above_pair;
+        s_eq = h1;
       } else {
         s_digit = 2 * tid;
         s_above = above_pair + h1;
+        s_eq = hist[2 * tid];
       }
     }
     __syncthreads();
@@ -105,6 +140,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   }
   const uint32_t kstar = prefix;
   const int n_gt = p.k - (int)need;  // keys above K*; `need` ties are taken
+  // After the last pass s_eq counts the keys equal to K*: when all of them
+  // are needed (the usual case) they join the first gather.
+  const bool all_ties = s_eq == need;
 
   // 2. Gather: every key above K* (any slot order: the sort fixes it), then
   // the `need` lowest-index keys equal to K*.
@@ -113,16 +151,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     s_taken = 0;
   }
   __syncthreads();
-  for (int i = tid; i < V; i += kSampleThreads) {
-    const float v = row[i];
-    if (fkey(v) > kstar) {
+  for_each_logit(row, V, tid, [&](float v, int i) {
+    const uint32_t key = fkey(v);
+    if (key > kstar || (all_ties && key == kstar)) {
       const uint32_t slot = atomicAdd(&s_count, 1u);
       cval[slot] = v;
       cidx[slot] = i;
     }
-  }
+  });
   __syncthreads();
-  for (int base = 0; base < V; base += kSampleThreads) {
+  for (int base = 0; !all_ties && base < V; base += kSampleThreads) {
     const uint32_t taken = s_taken;
     if (taken >= need) break;  // uniform: read after the barrier below
     const int i = base + tid;
