@@ -25,6 +25,7 @@ typedef _Float16 h16;
 typedef h16 h16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kNormThreads = 256;
+constexpr int kNormBwdThreads = 1024;  // 16 waves: four per SIMD keep more rows in flight
 
 // Pieces a lane may hold: a row of n / 8 pieces uses LPR = 64 lanes when it
 // has at least 64 pieces (then at most kNormMaxCols / 512 per lane), else the
@@ -92,14 +93,15 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_fwd_kernel(NormParams p)
   if (gl == 0) p.rstd_out[row] = r;
 }
 
-// Backward, one pass over the rows: dx per row, and this work-group's share
-// of dw. Row group grp of work-group g takes rows g GPW + grp + i n_wgs GPW
+// Backward, one pass over the rows with 1024-thread work-groups (GPW row
+// groups, four waves per SIMD): dx per row, and this work-group's share of
+// dw. Row group grp of work-group g takes rows g GPW + grp + i n_wgs GPW
 // (grid stride); every lane keeps fp32 dw sums for its pieces, then the
 // work-group adds its groups' sums through LDS in group order and writes one
 // partial row.
 template <int LPR>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_bwd_kernel(NormParams p) {
-  constexpr int GPW = kNormThreads / LPR;  // row groups per work-group
+__global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams p) {
+  constexpr int GPW = kNormBwdThreads / LPR;  // row groups per work-group
   constexpr int PPL = pieces_per_lane<LPR>();
   __shared__ float red[kNormMaxCols];
   const int lane = threadIdx.x & 63;
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_bwd_kernel(NormParams p)
     __syncthreads();
   }
   float* prow = p.part + (size_t)blockIdx.x * n;
-  for (int j = threadIdx.x; j < n; j += kNormThreads) prow[j] = red[j];
+  for (int j = threadIdx.x; j < n; j += kNormBwdThreads) prow[j] = red[j];
 }
 
 // dw_j = sum of the partial rows. A work-group owns 64 columns; its four
@@ -213,14 +215,14 @@ hipError_t launch_fwd_lpr(const NormParams& p, hipStream_t stream) {
 
 template <int LPR>
 hipError_t launch_bwd_lpr(const NormParams& p, int n_wgs, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel<LPR>, dim3(n_wgs), dim3(kNormThreads), 0, stream, p);
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel<LPR>, dim3(n_wgs), dim3(kNormBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int rmsnorm_bwd_num_wgs(int rows, int n) {
-  const int groups = kNormThreads / lanes_per_row(n);
+  const int groups = kNormBwdThreads / lanes_per_row(n);
   const int need = (rows + groups - 1) / groups;
   return need < 1 ? 1 : (need < kNormMaxWGs ? need : kNormMaxWGs);
 }

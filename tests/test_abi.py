@@ -253,8 +253,8 @@ def test_rmsnorm_argument_checks(lib):
     assert fwd(NormDims(10, 128), rstd=FAKE + 2) == INVALID
     assert fwd(NormDims(0, 128), x=0) == OK        # no rows: nothing to do
     need = lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(8192, 1024)))
-    assert need == min(8192 // 4, 256) * 1024 * 4  # a partial row per 4 rows, at most 256
-    assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(40, 1024))) == 10 * 4096
+    assert need == min(8192 // 16, 256) * 1024 * 4  # a partial row per 16 rows, at most 256
+    assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(40, 1024))) == 3 * 4096
     assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(1 << 20, 1024))) == \
         256 * 1024 * 4
     assert lib.attn_rmsnorm_bwd_workspace_bytes(ctypes.byref(NormDims(0, 1024))) == 0
