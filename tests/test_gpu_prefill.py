@@ -137,3 +137,47 @@ def test_prefill_empty_batches(gpu):
     torch.cuda.synchronize()
     assert o.shape[0] == 0 and lse.shape[1] == 0
     assert torch.equal(before, d["k_pool"])
+
+
+def _random_prefill_cases(n, seed):
+    """Seeded random chunked-prefill batches: 1-6 sequences, cached 0-700,
+    new 0-300 tokens, KV heads 1-4, group size 1-8, d 64 or 128."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        m = int(g.integers(1, 7))
+        prior = [int(x) for x in g.integers(0, 701, size=m)]
+        new = [int(x) for x in g.integers(0, 301, size=m)]
+        if sum(new) == 0:
+            new[0] = 1
+        h_kv = int(g.choice([1, 2, 4]))
+        G = int(g.choice([1, 2, 3, 4, 8]))
+        d = int(g.choice([64, 128]))
+        cases.append((prior, new, G * h_kv, h_kv, d, 5400 + i))
+    return cases
+
+
+@pytest.mark.parametrize("prior,new,h_q,h_kv,d,seed", _random_prefill_cases(8, 91),
+                         ids=lambda x: str(x))
+def test_prefill_random_batches(gpu, prior, new, h_q, h_kv, d, seed):
+    inp = W.poison_unused_prefill(W.make_prefill_inputs(prior, new, h_q, h_kv, d, seed=seed,
+                                                        spare_blocks=2))
+    name = f"prefill random seed {seed}"
+    print(name, flush=True)
+    dd, o, lse = _gpu(inp, gpu)
+    ref, kp, vp = _oracle(inp)
+    assert _same_bits(dd["k_pool"], torch.from_numpy(kp))
+    _check(name, inp, o, lse, ref)
+
+
+def test_prefill_one_token_chunks_match_decode(gpu):
+    """One new token per sequence: the prefill (forward kernel, paged) and the
+    decode (split-K gather) are different kernels computing the same row;
+    both must agree within the output bar."""
+    prior = [0, 15, 16, 100, 1000, 2047]
+    inp = W.make_prefill_inputs(prior, [1] * len(prior), 16, 8, 128, seed=5500)
+    dd, o, _ = _gpu(inp, gpu)
+    od = attn.decode_paged(dd["q"], dd["k_pool"], dd["v_pool"], dd["block_table"],
+                           dd["ctx_lens"], inp["scale"], max_ctx_len=inp["max_ctx"])
+    torch.cuda.synchronize()
+    assert max_abs(o.float().cpu().numpy(), od.float().cpu().numpy()) <= 2 * O_TOL

@@ -71,3 +71,11 @@ def test_sample_workload(gpu):
     rows = slice(0, 64)
     _check("rollout_sampling (64 rows)", inp["logits"][rows], inp["u"][rows],
            inp["temperature"], inp["top_k"], inp["top_p"], got[rows])
+
+
+def test_sample_small_top_p_keeps_the_top_token(gpu):
+    """A tiny top_p keeps only rank 0: the token is the argmax for every u."""
+    inp = W.make_sample_inputs(64, 5000, 2.0, seed=7100)
+    got = attn.sample(inp["logits"].to(gpu), inp["u"].to(gpu), 1.0, 50, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu().long(), inp["logits"].argmax(1))
