@@ -4,7 +4,10 @@
 //
 // One work-group of 1024 threads per row:
 //  1. radix select (11 + 11 + 10 bits of an order-preserving key of the fp32
-//     logit, one LDS histogram per pass) finds K*, the k-th largest key;
+//     logit, one LDS histogram per pass) finds K*, the k-th largest key; the
+//     first digit streams the row, then (when they fit) the keys past that
+//     digit are copied to LDS and the rest of the selection runs there, so
+//     the row is read twice instead of four times;
 //  2. the keys above K* are gathered (with the keys equal to K* when all of
 //     them are kept, the usual case; otherwise the lowest-index keys equal
 //     to K* follow, in tiles of 1024 in index order with ranks from wave
@@ -26,6 +29,7 @@ namespace {
 
 constexpr int kSampleThreads = 1024;
 constexpr int kWaves = kSampleThreads / 64;
+constexpr int kCandidates = 4096;  // LDS copy of the keys past the first radix digit
 
 struct SampleParams {
   const float* __restrict__ logits;
@@ -80,38 +84,30 @@ __device__ __forceinline__ void for_each_logit(const float* row, int V, int tid,
   for (int i = done + tid; i < V; i += kSampleThreads) fn(row[i], i);
 }
 
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t suf[kSampleThreads];
   __shared__ float cval[kMaxTopK];
   __shared__ int cidx[kMaxTopK];
   __shared__ float cum[kMaxTopK];
-  __shared__ uint32_t s_digit, s_above, s_eq, s_count, s_taken, s_wave[kWaves];
+  __shared__ uint32_t bkey[kCandidates];  // keys whose top digit reaches the k-th's
+  __shared__ int bidx[kCandidates];
+  __shared__ uint32_t s_digit, s_above, s_eq, s_count, s_taken, s_nb, s_wave[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int V = p.vocab;
   const float* row = p.logits + (size_t)blockIdx.x * V;
 
-  // 1. Radix select of the k-th largest key: digits of 11, 11 and 10 bits
-  // from the top; `need` is the rank of K* among the keys matching the
-  // digits chosen so far.
-  uint32_t prefix = 0, need = (uint32_t)p.k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int bits = pass == 2 ? 10 : 11;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + bits));
-    hist[2 * tid] = 0;
-    hist[2 * tid + 1] = 0;
-    __syncthreads();
-    for_each_logit(row, V, tid, [&](float x, int) {
-      const uint32_t key = fkey(x);
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
-    });
-    __syncthreads();
-    // Suffix sums over digit pairs (2t, 2t + 1), then the pair and digit
-    // where the count of larger digits first reaches `need`.
+  // Digit of the histogram where the count of larger digits first reaches
+  // `need`: suffix sums over digit pairs (2t, 2t + 1), then the pair's digit.
+  // Sets s_digit, s_above (keys with larger digits) and s_eq (keys with
+  // this digit).
+  auto find_digit = [&](uint32_t need) {
     suf[tid] = hist[2 * tid] + hist[2 * tid + 1];
     __syncthreads();
     for (int off = 1; off < kSampleThreads; off <<= 1) {
@@ -134,31 +130,88 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
       }
     }
     __syncthreads();
+  };
+  auto clear_hist = [&]() {
+    hist[2 * tid] = 0;
+    hist[2 * tid + 1] = 0;
+    __syncthreads();
+  };
+
+  // 1. Radix select of the k-th largest key: digits of 11, 11 and 10 bits
+  // from the top; `need` is the rank of K* among the keys matching the
+  // digits chosen so far. The first digit streams the row; when the keys
+  // whose first digit reaches the chosen one fit in LDS (kCandidates), one
+  // more pass copies them there and the other digits (and the gather) work
+  // on that copy instead of re-reading the row.
+  clear_hist();
+  for_each_logit(row, V, tid, [&](float x, int) { atomicAdd(&hist[fkey(x) >> 21], 1u); });
+  __syncthreads();
+  find_digit((uint32_t)p.k);
+  uint32_t prefix = s_digit << 21;
+  uint32_t need = (uint32_t)p.k - s_above;
+  const bool buffered = s_above + s_eq <= (uint32_t)kCandidates;  // uniform
+  __syncthreads();
+  if (buffered) {
+    if (tid == 0) s_nb = 0;
+    __syncthreads();
+    const uint32_t d1 = prefix >> 21;
+    for_each_logit(row, V, tid, [&](float x, int i) {
+      const uint32_t key = fkey(x);
+      if ((key >> 21) >= d1) {
+        const uint32_t slot = atomicAdd(&s_nb, 1u);
+        bkey[slot] = key;
+        bidx[slot] = i;
+      }
+    });
+    __syncthreads();
+  }
+  const int nb = buffered ? (int)s_nb : 0;
+#pragma unroll 1
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
+    const int bits = pass == 2 ? 10 : 11;
+    const uint32_t hi_mask = 0xFFFFFFFFu << (shift + bits);
+    clear_hist();
+    auto count = [&](uint32_t key) {
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
+    };
+    if (buffered) {
+      for (int j = tid; j < nb; j += kSampleThreads) count(bkey[j]);
+    } else {
+      for_each_logit(row, V, tid, [&](float x, int) { count(fkey(x)); });
+    }
+    __syncthreads();
+    find_digit(need);
     prefix |= s_digit << shift;
     need -= s_above;
     __syncthreads();
   }
   const uint32_t kstar = prefix;
   const int n_gt = p.k - (int)need;  // keys above K*; `need` ties are taken
-  // After the last pass s_eq counts the keys equal to K*: when all of them
-  // are needed (the usual case) they join the first gather.
-  const bool all_ties = s_eq == need;
+  // s_eq now counts the keys equal to K*. When they all fit next to the keys
+  // above K*, every one joins the gather and the sort keeps the lowest
+  // indices (the usual case); otherwise the `need` lowest-index ties are
+  // taken in index order below.
+  const bool all_ties = n_gt + s_eq <= (uint32_t)kMaxTopK;
 
-  // 2. Gather: every key above K* (any slot order: the sort fixes it), then
-  // the `need` lowest-index keys equal to K*.
+  // 2. Gather.
   if (tid == 0) {
     s_count = 0;
     s_taken = 0;
   }
   __syncthreads();
-  for_each_logit(row, V, tid, [&](float v, int i) {
-    const uint32_t key = fkey(v);
+  auto take = [&](uint32_t key, int i) {
     if (key > kstar || (all_ties && key == kstar)) {
       const uint32_t slot = atomicAdd(&s_count, 1u);
-      cval[slot] = v;
+      cval[slot] = key_to_float(key);
       cidx[slot] = i;
     }
-  });
+  };
+  if (buffered) {
+    for (int j = tid; j < nb; j += kSampleThreads) take(bkey[j], bidx[j]);
+  } else {
+    for_each_logit(row, V, tid, [&](float x, int i) { take(fkey(x), i); });
+  }
   __syncthreads();
   for (int base = 0; !all_ties && base < V; base += kSampleThreads) {
     const uint32_t taken = s_taken;
@@ -184,8 +237,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     }
     __syncthreads();
   }
-  // Unused slots sort last.
-  if (tid >= p.k) {
+  // Unused slots sort last (with every tie gathered there can be more than
+  // k filled slots; the sort puts the first k of the ranking in front).
+  const int filled = all_ties ? (int)s_count : p.k;
+  if (tid >= filled) {
     cval[tid] = -INFINITY;
     cidx[tid] = 0x7FFFFFFF;
   }

@@ -262,13 +262,13 @@ def norm_workload_inputs(name):
     return make_norm_inputs(w["rows"], w["n"], w["seed"])
 
 
-def make_sample_inputs(n, vocab, scale, seed, step=None, masked=0.0):
-    """Logits [n, vocab] = scale N(0,1) in fp32 (rounded to multiples of
+def make_sample_inputs(n, vocab, scale, seed, step=None, masked=0.0, offset=0.0):
+    """Logits [n, vocab] = offset + scale N(0,1) in fp32 (rounded to multiples of
     `step` when given, which creates ties; a `masked` fraction set to -inf,
     never the first entry of a row) and uniforms u [n] in [0, 1). Draw
     order: logits, mask, u."""
     g = _gen(seed)
-    logits = torch.randn(n, vocab, generator=g, dtype=torch.float32) * scale
+    logits = torch.randn(n, vocab, generator=g, dtype=torch.float32) * scale + offset
     if step:
         logits = torch.round(logits / step) * step
     if masked > 0:

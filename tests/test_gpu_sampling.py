@@ -29,6 +29,7 @@ CASES = [
     (64, 3000, 64, 0.9, 1.0, 2.0, 0.5, 0.0),     # many exact ties, also at the k-th value
     (32, 4096, 100, 1.0, 0.8, 2.0, None, 0.99),  # mostly -inf: fewer finite logits than k
     (16, 151936, 20, 0.95, 0.6, 3.0, None, 0.0),
+    (4, 20000, 1024, 1.0, 1.0, 1.0, 1.0, 0.0),     # integer logits: > 1024 ties at the k-th value
 ]
 
 
@@ -59,6 +60,15 @@ def test_sample_cases(gpu, n, V, k, tp, T, scale, step, masked):
     got = attn.sample(inp["logits"].to(gpu), inp["u"].to(gpu), T, k, tp)
     torch.cuda.synchronize()
     _check(f"sample n{n} V{V} k{k} p{tp} T{T}", inp["logits"], inp["u"], T, k, tp, got)
+
+
+def test_sample_without_the_lds_copy(gpu):
+    """Logits 1 + 1e-3 N(0,1) share one first radix digit, so more keys than
+    the LDS copy holds reach the k-th one: the selection re-reads the row."""
+    inp = W.make_sample_inputs(8, 151936, 1e-3, seed=7200, offset=1.0)
+    got = attn.sample(inp["logits"].to(gpu), inp["u"].to(gpu), 1e-3, 512, 0.9)
+    torch.cuda.synchronize()
+    _check("sample unbuffered", inp["logits"], inp["u"], 1e-3, 512, 0.9, got)
 
 
 def test_sample_workload(gpu):
