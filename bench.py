@@ -15,7 +15,10 @@ per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
 bounded sample of the same training workload. ``prefill`` times the rollout
 engine's chunked prefill (attn_kv_append + attn_prefill_paged on the
 paged_prefill workload) separately, after the timed steps; it is not part of
-``value``. ``rmsnorm`` likewise times RMSNorm forward and backward on the
+``value``. ``measured_peaks`` holds this GPU's measured dense fp16 MFMA rate,
+the shader clock under it and its streaming-read rate (probe kernels of
+libattn_probe.so), the second denominators beside the published peaks.
+``rmsnorm`` likewise times RMSNorm forward and backward on the
 training batch's layer norm and per-head query norm (HBM-bound, GB/s), and
 ``sampling`` the rollout batch's temperature / top-k / top-p sampling.
 
@@ -38,7 +41,8 @@ HBM_PEAK_GBPS = 8000.0
 TRAIN_WORKLOAD = "qwen3_train"
 DECODE_WORKLOAD = "paged_decode"
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
-                  "attn_norm.hip", "attn_sample.hip", "cdna4.h", "kernels.h", "attn_api.cpp"]
+                  "attn_norm.hip", "attn_sample.hip", "probe_peaks.hip", "cdna4.h", "kernels.h",
+                  "attn_api.cpp"]
 
 
 def causal_pairs(seqlens):
@@ -262,6 +266,65 @@ def bench_sampling(attn, W, dev, iters):
             "hbm_peak_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def measured_peaks(dev):
+    """Second denominators measured on this GPU by the probe library
+    (libattn_probe.so): dense fp16 MFMA rate of independent 32x32x16 chains
+    (1024 work-groups of 4 waves, 8 chains each) with the shader clock under
+    that load, and the streaming-read rate of 16-byte non-temporal loads over
+    2 GiB. Best of three runs each; None if the probe library is not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "causal_gqa_attention_fa2_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.probe_mfma_flops.restype = ctypes.c_double
+    lib.probe_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.probe_mfma_f16.restype = ctypes.c_int
+    lib.probe_stream_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    lib.probe_stream_read.restype = ctypes.c_int
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    n_wg, iters = 1024, 2000
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        fn()
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e-3
+
+    best_mfma, clock_ghz = 0.0, None
+    for _ in range(3):
+        t = timed(lambda: lib.probe_mfma_f16(n_wg, iters, vp(out.data_ptr()),
+                                             vp(clocks.data_ptr()), stream))
+        rate = lib.probe_mfma_flops(n_wg, iters) / t / 1e12
+        if rate > best_mfma:
+            best_mfma = rate
+            ticks, real = (int(x) for x in clocks.cpu())
+            clock_ghz = ticks / (real / 100e6) / 1e9 if real > 0 else None
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rwg = 4096
+    rout = torch.empty(rwg * 256, dtype=torch.int32, device=dev)
+    best_read = 0.0
+    for _ in range(3):
+        t = timed(lambda: lib.probe_stream_read(vp(buf.data_ptr()), nbytes, rwg,
+                                                vp(rout.data_ptr()), stream))
+        best_read = max(best_read, nbytes / t / 1e9)
+    del buf
+    return {"mfma_f16_tflops": round(best_mfma, 1),
+            "shader_clock_ghz_under_mfma": round(clock_ghz, 3) if clock_ghz else None,
+            "stream_read_gbps": round(best_read, 1),
+            "how": "probe_peaks.hip: 1024 x 4 waves x 8 independent 32x32x16 fp16 MFMA chains; "
+                   "16-byte non-temporal reads of 2 GiB, 8 in flight per thread; best of 3"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +332,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak probes (MFMA rate, streaming read)")
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="untimed steady-state run before the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -396,6 +461,11 @@ def main():
         "roofline": roofline,
         "source_digest": source_digest(),
     }
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    if peaks:
+        out["measured_peaks"] = peaks
+        out["mfma_measured_frac"] = round(tflops / peaks["mfma_f16_tflops"], 4)
+        out["decode"]["hbm_measured_frac"] = round(dec_gbps / peaks["stream_read_gbps"], 4)
     out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
     out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
     out["sampling"] = bench_sampling(attn, W, dev, max(args.steps, 5))

@@ -1,4 +1,5 @@
-"""Build libattn.so (the C-ABI attention library) in-tree for gfx950.
+"""Build libattn.so (the C-ABI attention library) and libattn_probe.so (the
+benchmark's peak-measurement kernels) in-tree for gfx950.
 
 Usage: ``python -m causal_gqa_attention_fa2_amd.build`` or ``build()``.
 Each source compiles to an object under ``_build/`` (in parallel), then
@@ -16,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
+# Measurement kernels (measured MFMA and HBM peaks), loaded by the benchmark only.
+PROBE_SOURCE = "probe_peaks.hip"
+PROBE_LIB_PATH = os.path.join(PKG, "libattn_probe.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
            "attn_norm.hip", "attn_sample.hip"]
@@ -69,6 +73,13 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"hipcc link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    probe_obj = _compile(PROBE_SOURCE, verbose)
+    tmp = PROBE_LIB_PATH + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc link failed (probe):\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB_PATH)
     return LIB_PATH
 
 
