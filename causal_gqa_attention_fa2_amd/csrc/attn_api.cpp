@@ -58,7 +58,15 @@ attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
 size_t bwd_row_bytes(const attn_varlen_dims* d) {
   return align_up((size_t)d->h_q * d->total_tokens * sizeof(float));
 }
-size_t bwd_ws_bytes(const attn_varlen_dims* d) { return 2 * bwd_row_bytes(d); }
+bool bwd_ds_path(const attn_varlen_dims* d) {
+  return cgqa::bwd_use_ds(d->n_seqs, d->total_tokens, d->max_seqlen, d->h_q);
+}
+size_t bwd_ds_bytes(const attn_varlen_dims* d) {
+  return bwd_ds_path(d)
+             ? align_up(cgqa::bwd_ds_blocks(d->n_seqs, d->h_q, d->max_seqlen) * cgqa::kDsBlockBytes)
+             : 0;
+}
+size_t bwd_ws_bytes(const attn_varlen_dims* d) { return 2 * bwd_row_bytes(d) + bwd_ds_bytes(d); }
 
 attn_status check_paged(const attn_paged_dims* d, bool* empty) {
   if (!d) return ATTN_ERR_INVALID_ARG;
@@ -197,6 +205,7 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.dv = dv;
   a.drow = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + bwd_row_bytes(dims));
+  a.ds = bwd_ds_path(dims) ? (char*)workspace + 2 * bwd_row_bytes(dims) : nullptr;
   a.n_seqs = dims->n_seqs;
   a.total_tokens = dims->total_tokens;
   a.max_seqlen = dims->max_seqlen;

@@ -33,6 +33,13 @@
 // tile size) but drops the fp32 dQ accumulator, its zeroing, its conversion
 // pass and all atomic traffic.
 //
+// Batches of very unequal sequence lengths take a second path (chosen by
+// the host from the batch shape, with a larger workspace): a row-term
+// kernel, then dK/dV that also stores each fp16 dS block, then a dQ kernel
+// that reads those blocks instead of recomputing S and dP (5 GEMMs of the
+// tile size plus the dS traffic). There the short work items make the
+// recomputing dq kernel's per-item costs dominate.
+//
 // Tiles reach LDS through direct global-to-LDS copies issued two tiles ahead
 // (cdna4.h dma16/dma4), one barrier per tile. Every tile uses the chunk
 // swizzle of cdna4.h, so row reads and transpose reads are free of bank
@@ -65,6 +72,8 @@ struct BwdParams {
   f16* __restrict__ dq;
   f16* __restrict__ dk;
   f16* __restrict__ dv;
+  f16* __restrict__ ds;      // workspace: fp16 dS blocks (32 x 32, lane-major)
+  int nbmax;                 // 32-row blocks of the longest sequence
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles, n_ktiles;
   float scale, scale_log2;
 };
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool STORE_DS>
 __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NT = D / 16;
   constexpr int ND = D / 32;
@@ -444,6 +453,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
 
+  // Team 1's dS block of query block m (32 rows x the pair's 32 keys) to the
+  // workspace for the dQ kernel, lane-major: lane l's 16 values (rows
+  // 8(i/4) + 4hi + i%4 of key column l % 32) at halves 16 l .. 16 l + 15.
+  // Pairs wholly past the sequence store nothing. The stores count in vmcnt,
+  // so the next iteration's copy wait also waits for them.
+  auto store_ds = [&](int m, const f16x8* f) {
+    if (kw0 >= L) return;
+    const int head = g * p.G + m / n_qb;
+    const int qb = qb_begin + m % n_qb;
+    f16* dst = p.ds + ((((size_t)b * p.h_q + head) * p.nbmax + qb) * p.nbmax + (kw0 >> 5)) * 1024 +
+               lane * 16;
+    *(f16x8*)dst = f[0];
+    *(f16x8*)(dst + 8) = f[1];
+  };
+
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): see dq_kernel
   if (n_it > 1) issue_blk(1, 1);
   for (int j = 0; j <= n_it; ++j) {
@@ -512,8 +536,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
       // block; every other block takes the unmasked copy of the loop (two
       // copies, so the compiler does not evaluate the mask everywhere).
       if (kw0 + 31 > q0 || q0 + 31 >= L) {
-        // Keep P where key <= row < L, i.e. 0 <= row - key < L - key.
-        const int lim = L - key;
+        // Keep P where key <= row < L, i.e. 0 <= row - key < L - key. Keys
+        // past the sequence (lim <= 0) keep nothing, so their dS is zero.
+        const int lim = max(L - key, 0);
         const int rel = q0 + 4 * hi - key;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -534,6 +559,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
         const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
         f[i >> 3][i & 7] = (f16)(pv * (sa[i] - l4[i >> 2][i & 3]));
       }
+      if constexpr (STORE_DS) store_ds(m, f);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -561,6 +587,223 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   }
 }
 
+
+// Row terms of the backward for every (token, query head) row: D = rowsum(dO
+// * O) and LSE * log2(e), stored [h_q, T]. A group of D/8 lanes owns a row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;  // rows per work-group and pass
+  const int tid = threadIdx.x;
+  const int gl = tid % LPR;
+  const int n = p.T * p.h_q;  // < 2^31
+  for (int row = blockIdx.x * RPB + tid / LPR; row < n; row += gridDim.x * RPB) {  // t * h_q + h
+    const f16x8 ov = *(const f16x8*)(p.o + (size_t)row * D + 8 * gl);
+    const f16x8 gv = *(const f16x8*)(p.dout + (size_t)row * D + 8 * gl);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)gv[e] * (float)ov[e];
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (gl == 0) {
+      const int t = row / p.h_q;
+      const int h = row - t * p.h_q;
+      const size_t i = (size_t)h * p.T + t;
+      p.drow[i] = acc;
+      p.lse2[i] = p.lse[i] * kLog2e;
+    }
+  }
+}
+
+// dQ from the dS blocks the dK/dV kernel stored: dQ^T += K^T dS^T over the
+// 32-key blocks at or before each query block. Work items, persistent
+// XCD-aware work-groups and the three-stage ring are those of dq_kernel; a
+// ring stage holds the K tile (chunk swizzle) and each wave's own dS block
+// (2 KiB, copied as stored). Operands come from LDS transpose reads in
+// natural key order: k-step u, half hi, slot s <-> key 16u + 8hi + s, both
+// for K^T (rows of the K tile) and for dS^T (the stored block's lanes
+// 32 hi' + key hold rows 8c + 4hi' + 0..3 in their 8-byte chunk c).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
+  constexpr int ND = D / 32;
+  constexpr int CH = D / 8;
+  constexpr int RPI = 64 / CH;
+  constexpr int NI = kDqBC * CH / 64;  // K copy instructions per tile (8 or 4)
+  static_assert(NI >= 1 && 8 % NI == 0, "K tile must split over the waves");
+  constexpr int CPW = 3;               // copies per wave and tile: one K, two dS
+  constexpr int TILE = kDqBC * D;
+  constexpr int STAGE = TILE + 8 * 1024;
+  __shared__ __attribute__((aligned(16))) f16 smem[kDqStages * STAGE];
+  static_assert(kDqStages == 3, "the ring below has three stages");
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int grp = lane >> 4;
+  const int j16 = lane & 15;
+
+  constexpr int kXcds = 8;
+  const int BR = 32 * p.nqb;
+  const int per = p.n_seqs * p.h_kv * p.n_chunks;
+  const int n_items = p.n_qtiles * per;
+  const int NW = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
+  const int xcd = w % kXcds;
+  const int wx = w / kXcds;
+  const int nwx = (NW - xcd + kXcds - 1) / kXcds;
+  auto item_of = [&](int r) {
+    const int j = r * nwx + ((r & 1) ? nwx - 1 - wx : wx);
+    return xcd + kXcds * j;
+  };
+  struct Item {
+    int b, g, chunk, s0, L, q_wg0, n_kt;
+  };
+  auto decode = [&](int i) {
+    Item it;
+    const int qt = p.n_qtiles - 1 - i / per;
+    int rem = i % per;
+    it.chunk = rem % p.n_chunks;
+    rem /= p.n_chunks;
+    it.g = rem % p.h_kv;
+    it.b = rem / p.h_kv;
+    it.s0 = load_uniform(p.cu, it.b);
+    it.L = load_uniform(p.cu, it.b + 1) - it.s0;
+    it.q_wg0 = qt * BR;
+    it.n_kt = it.q_wg0 < it.L ? (min(it.L, it.q_wg0 + BR) + kDqBC - 1) / kDqBC : 0;
+    return it;
+  };
+  auto next_item = [&](int& r) {
+    for (;; ++r) {
+      const int i = item_of(r);
+      if (i >= n_items) return n_items;
+      if (decode(i).n_kt > 0) return i;
+    }
+  };
+  struct Rows {
+    int head, q0, qpos, qrow;
+    bool has_rows, valid;
+    const f16* dsb;  // this wave's dS blocks: query block row of the workspace
+    int qbc;         // its query block, clamped into the sequence
+  };
+  auto rows_of = [&](const Item& it) {
+    Rows rw;
+    const int hig = it.chunk * p.hpw + wave / p.nqb;
+    rw.head = it.g * p.G + min(hig, p.G - 1);
+    rw.q0 = it.q_wg0 + (wave % p.nqb) * 32;
+    rw.qpos = rw.q0 + l32;
+    rw.has_rows = rw.q0 < it.L && hig < p.G;
+    rw.valid = rw.qpos < it.L && hig < p.G;
+    rw.qrow = it.s0 + min(rw.qpos, it.L - 1);
+    rw.qbc = min(rw.q0 >> 5, (it.L - 1) >> 5);
+    rw.dsb = p.ds + (((size_t)it.b * p.h_q + rw.head) * p.nbmax + rw.qbc) * p.nbmax * 1024;
+    return rw;
+  };
+  // Copies of tile kt into stage st: one K instruction per wave (rows of
+  // instruction wave % NI; with NI < 8 two waves write the same rows with the
+  // same data) and this wave's dS block for key block kt, clamped to a block
+  // that exists so every wave issues the same number of copies.
+  auto issue_tile = [&](const Item& it, const Rows& rw, int kt, int st) {
+    f16* stage = smem + st * STAGE;
+    const int ii = wave % NI;
+    const int r = ii * RPI + lane / CH;
+    const int sl = (lane % CH) * 8;
+    const size_t row = ((size_t)(it.s0 + min(kt * kDqBC + r, it.L - 1)) * p.h_kv + it.g) * D;
+    dma16(p.k + row + swz<D>(r, sl), stage + ii * 512);
+    const f16* src = rw.dsb + (size_t)min(kt, rw.qbc) * 1024 + lane * 8;
+    dma16(src, stage + TILE + wave * 1024);
+    dma16(src + 512, stage + TILE + wave * 1024 + 512);
+  };
+
+  // Per-lane LDS offsets (halves). K^T: rows 8hi + 4r + j16/4 (+ 16u),
+  // columns 32db + 16(grp&1) + 4(j16&3). dS^T: lane 4e + jj of group grp
+  // reads the chunk of stored lane 32 (jj&1) + 16u + 8(grp>>1) + 4r + e,
+  // chunk 2(grp&1) + jj/2.
+  int kto[2][ND];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int row = 8 * hi + 4 * r + (j16 >> 2);
+      kto[r][db] = row * D + swz<D>(row, 32 * db + 16 * (grp & 1) + 4 * (j16 & 3));
+    }
+  }
+  int dso[2][2];
+  {
+    const int e = j16 >> 2, jj = j16 & 3;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        dso[u][r] = (32 * (jj & 1) + 16 * u + 8 * (grp >> 1) + 4 * r + e) * 16 +
+                    4 * (2 * (grp & 1) + (jj >> 1));
+    }
+  }
+
+  int round = 0;
+  int cur = next_item(round);
+  if (cur >= n_items) return;
+  Item it = decode(cur);
+  Rows rw = rows_of(it);
+  issue_tile(it, rw, 0, 0);
+
+  for (;;) {
+    f32x16 acc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[db] = zero_f32x16();
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    const int n_kt = it.n_kt;
+    if (n_kt > 1) issue_tile(it, rw, 1, 1);
+    auto step = [&](int kt, auto S) __attribute__((always_inline)) {
+      constexpr int st = decltype(S)::value;
+      if (kt + 1 < n_kt) wait_vm_barrier<CPW>();
+      else wait_vm_barrier<0>();
+      if (kt + 2 < n_kt) issue_tile(it, rw, kt + 2, (st + 2) % kDqStages);
+      if (!rw.has_rows || kt * kDqBC > rw.q0 + 31) return;  // no keys of this tile are seen
+      const f16* Kb = smem + st * STAGE;
+      const f16* Db = Kb + TILE + wave * 1024;
+      f16x8 dsf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dsf[u] = cat4(lds_read_tr(Db + dso[u][0]), lds_read_tr(Db + dso[u][1]));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const f16x8 kt8 = cat4(lds_read_tr(Kb + kto[0][db] + 16 * u * D),
+                                 lds_read_tr(Kb + kto[1][db] + 16 * u * D));
+          acc[db] = mfma32x32x16(kt8, dsf[u], acc[db]);
+        }
+      }
+    };
+    for (int kt = 0; kt < n_kt; kt += kDqStages) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
+    }
+    if (rw.valid) {
+      f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f16x4 wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[e] = (f16)(acc[db][4 * r4 + e] * p.scale);
+          *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = wv;
+        }
+      }
+    }
+    lds_barrier();
+    ++round;
+    const int nxt = next_item(round);
+    if (nxt >= n_items) break;
+    it = decode(nxt);
+    rw = rows_of(it);
+    issue_tile(it, rw, 0, 0);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -574,6 +817,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.cu = a.cu_seqlens;
   p.drow = a.drow;
   p.lse2 = a.lse2;
+  p.ds = (f16*)a.ds;
+  p.nbmax = (a.max_seqlen + 31) / 32;
   p.dq = (f16*)a.dq;
   p.dk = (f16*)a.dk;
   p.dv = (f16*)a.dv;
@@ -592,16 +837,33 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.n_ktiles = (a.max_seqlen + kBK - 1) / kBK;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  // dq: persistent, at most one work-group per compute unit.
   const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
-  const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);
+  const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);  // persistent dq grids
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL(dq_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
-    hipLaunchKernelGGL(dkdv_kernel<128>, gk, dim3(kBwdThreads), 0, stream, p);
+  if (a.ds == nullptr) {
+    // Recompute path: dq (which also forms the row terms) then dK/dV.
+    if (a.head_dim == 128) {
+      hipLaunchKernelGGL(dq_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<128, false>), gk, dim3(kBwdThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(dq_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<64, false>), gk, dim3(kBwdThreads), 0, stream, p);
+    }
   } else {
-    hipLaunchKernelGGL(dq_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
-    hipLaunchKernelGGL(dkdv_kernel<64>, gk, dim3(kBwdThreads), 0, stream, p);
+    // dS path: row terms, then dK/dV (which also stores dS), then dQ from dS.
+    const long long rows = (long long)a.total_tokens * a.h_q;
+    const int rpb = 256 / (a.head_dim / 8);
+    const long long wgs = (rows + rpb - 1) / rpb;
+    const dim3 gr((unsigned)(wgs < 4 * a.num_cus ? wgs : 4 * a.num_cus));
+    if (a.head_dim == 128) {
+      hipLaunchKernelGGL(bwd_rows_kernel<128>, gr, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<128, true>), gk, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL(dq_ds_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(bwd_rows_kernel<64>, gr, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<64, true>), gk, dim3(kBwdThreads), 0, stream, p);
+      hipLaunchKernelGGL(dq_ds_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

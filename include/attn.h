@@ -110,7 +110,11 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
 
 /* Bytes of device workspace attn_bwd needs for `dims` (0 for an empty
  * batch). Holds two fp32 [h_q, T] arrays of per-row terms: D = rowsum(dO * O)
- * and LSE * log2(e). */
+ * and LSE * log2(e). For batches of very unequal lengths (n_seqs >= 2 and
+ * n_seqs * max_seqlen >= 1.25 total_tokens) it also holds fp16 dS blocks,
+ * n_seqs * h_q * ceil(max_seqlen / 32)^2 * 2 KiB (when that is at most
+ * 4 GiB): the backward then stores dS once instead of recomputing it for dQ.
+ * The result depends on dims only. */
 size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims);
 
 /*

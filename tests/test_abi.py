@@ -83,6 +83,12 @@ def test_bwd_workspace(lib):
     row = (16 * 100 * 4 + 255) // 256 * 256
     assert need == 2 * row
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(0, 0, 0, 16, 8, 128))) == 0
+    # Very unequal lengths (4 * 60 >= 1.25 * 100): room for the fp16 dS blocks too.
+    ragged = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(4, 100, 60, 16, 8, 128)))
+    assert ragged == 2 * row + 4 * 16 * 2 * 2 * 32 * 32 * 2
+    # Equal lengths keep the recompute path and its small workspace.
+    eq = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(8, 8192, 1024, 16, 8, 128)))
+    assert eq == 2 * ((16 * 8192 * 4 + 255) // 256 * 256)
     p = ctypes.c_void_p
     args = [p(FAKE)] * 7 + [p(FAKE)] * 3
 
