@@ -353,8 +353,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int CH = D / 8;
   constexpr int RPI = 64 / CH;
   constexpr int IPB = 32 * CH / 64;  // copy instructions per 32-row block of one tensor
-  constexpr int CPW = 2 * IPB / 8;   // copy instructions per wave per block (Q and dO)
-  static_assert(CPW >= 1 && 2 * IPB == 8 * CPW, "block must split over the waves");
+  // Team 0 issues every copy (team 1 issues none, so its vmcnt counts only
+  // its own dS stores and it never waits for them at the ring barrier).
+  constexpr int CPW = 2 * IPB / 4;   // copy instructions per team-0 wave per block (Q and dO)
+  static_assert(CPW >= 1 && 2 * IPB == 4 * CPW, "block must split over team 0");
   constexpr int BLK = 32 * D;
   // Ring of query blocks: [stage][Q, dO] tiles (chunk swizzle) and, per
   // stage, LSE * log2(e) (32 floats) then D (32 floats) of the block's rows.
@@ -398,11 +400,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   // row terms. Rows past the sequence fetch its last row; the mask below
   // zeroes their weights.
   auto issue_blk = [&](int m, int st) {
+    if (team != 0) return;
     const int head = g * p.G + m / n_qb;
     const int q0 = (qb_begin + m % n_qb) * 32;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int i = wave * CPW + c;
+      const int i = w4 * CPW + c;
       const int tsel = i / IPB;
       const int ii = i % IPB;
       const int r = ii * RPI + lane / CH;
@@ -474,7 +477,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     // Block j has landed for every wave (block j + 1 may still be in
     // flight), every wave is done with its block of the previous iteration,
     // and team 0's P of block j - 1 is in LDS.
-    if (j + 1 < n_it) {
+    if (team == 1) {
+      lds_barrier();  // no copies of its own; its dS stores stay in flight
+    } else if (j + 1 < n_it) {
       if (wave == 0) wait_vm_barrier<CPW + 1>();
       else wait_vm_barrier<CPW>();
     } else {
