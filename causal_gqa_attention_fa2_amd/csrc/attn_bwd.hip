@@ -599,23 +599,37 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;  // rows per work-group and pass
+  constexpr int kU = 4;           // rows per group in flight
   const int tid = threadIdx.x;
   const int gl = tid % LPR;
   const int n = p.T * p.h_q;  // < 2^31
-  for (int row = blockIdx.x * RPB + tid / LPR; row < n; row += gridDim.x * RPB) {  // t * h_q + h
-    const f16x8 ov = *(const f16x8*)(p.o + (size_t)row * D + 8 * gl);
-    const f16x8 gv = *(const f16x8*)(p.dout + (size_t)row * D + 8 * gl);
-    float acc = 0.f;
+  const int stride = gridDim.x * RPB;
+  for (int row0 = blockIdx.x * RPB + tid / LPR; row0 < n; row0 += kU * stride) {
+    f16x8 ov[kU], gv[kU];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)gv[e] * (float)ov[e];
+    for (int u = 0; u < kU; ++u) {
+      const int row = row0 + u * stride;  // t * h_q + h
+      if (row < n) {
+        ov[u] = *(const f16x8*)(p.o + (size_t)row * D + 8 * gl);
+        gv[u] = *(const f16x8*)(p.dout + (size_t)row * D + 8 * gl);
+      }
+    }
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (gl == 0) {
-      const int t = row / p.h_q;
-      const int h = row - t * p.h_q;
-      const size_t i = (size_t)h * p.T + t;
-      p.drow[i] = acc;
-      p.lse2[i] = p.lse[i] * kLog2e;
+    for (int u = 0; u < kU; ++u) {
+      const int row = row0 + u * stride;
+      if (row >= n) break;  // uniform over the group
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)gv[u][e] * (float)ov[u][e];
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+      if (gl == 0) {
+        const int t = row / p.h_q;
+        const int h = row - t * p.h_q;
+        const size_t i = (size_t)h * p.T + t;
+        p.drow[i] = acc;
+        p.lse2[i] = p.lse[i] * kLog2e;
+      }
     }
   }
 }
