@@ -25,6 +25,8 @@ of masked softmax attention, evaluated naively in float64:
   RMSNorm, the layer operation next to attention, and its backward.
 * ``sample_ref`` (module ``oracle.sampling``) -- temperature / top-k / top-p
   sampling over logits with a caller-supplied uniform.
+* ``rope_ref`` and ``rope_tables_ref`` (module ``oracle.rope``) -- rotary
+  position embedding of q and k and its inverse (the backward).
 
 Every function is pinned by tests that do not re-use its formulas: closed
 forms, invariants, finite differences, a hand-derived worked example and
@@ -40,3 +42,10 @@ from .attention import (  # noqa: F401
 )
 from .rmsnorm import rmsnorm_bwd_ref, rmsnorm_fwd_ref  # noqa: F401,E402
 from .sampling import sample_ref  # noqa: F401,E402
+from .rope import (  # noqa: F401,E402
+    chunk_positions,
+    rope_fp16_ref,
+    rope_ref,
+    rope_tables_ref,
+    varlen_positions,
+)
