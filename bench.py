@@ -19,8 +19,10 @@ paged_prefill workload) separately, after the timed steps; it is not part of
 the shader clock under it and its streaming-read rate (probe kernels of
 libattn_probe.so), the second denominators beside the published peaks.
 ``rmsnorm`` likewise times RMSNorm forward and backward on the
-training batch's layer norm and per-head query norm (HBM-bound, GB/s), and
-``sampling`` the rollout batch's temperature / top-k / top-p sampling.
+training batch's layer norm and per-head query norm (HBM-bound, GB/s),
+``sampling`` the rollout batch's temperature / top-k / top-p sampling, and
+``rope`` the rotary embedding pass over the training batch's q and k plus
+the append and prefill with the rotation fused in.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -41,8 +43,8 @@ HBM_PEAK_GBPS = 8000.0
 TRAIN_WORKLOAD = "qwen3_train"
 DECODE_WORKLOAD = "paged_decode"
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
-                  "attn_norm.hip", "attn_sample.hip", "probe_peaks.hip", "cdna4.h", "kernels.h",
-                  "attn_api.cpp"]
+                  "attn_norm.hip", "attn_sample.hip", "attn_rope.hip", "probe_peaks.hip", "cdna4.h",
+                  "kernels.h", "attn_api.cpp"]
 
 
 def causal_pairs(seqlens):
@@ -189,6 +191,59 @@ def bench_prefill(attn, W, dev, iters):
             "attn_us": round(t_att * 1e6, 2),
             "attn_TFLOP/s": round(flops / t_att / 1e12, 2),
             "attn_mfma_peak_frac": round(flops / t_att / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
+def bench_rope(attn, W, dev, iters):
+    """RoPE, timed on its own (not part of `value`): the standalone pass over
+    the training batch's q and k (qwen3_train: 8 x 1024 tokens, 16 + 8 heads,
+    d = 128), forward and inverse, HBM-bound against 8 TB/s; and on the
+    paged_prefill workload the append and the prefill with the rotation
+    fused in, beside the same calls without it."""
+    import torch
+    inp = W.workload_inputs(TRAIN_WORKLOAD, with_dout=False)
+    q, k, cu = inp["q"].to(dev), inp["k"].to(dev), inp["cu_seqlens"].to(dev)
+    T, h_q, d = q.shape
+    h_kv = k.shape[1]
+    pre = W.prefill_workload_inputs(PREFILL_WORKLOAD)
+    max_pos = max(inp["max_seqlen"], pre["max_ctx"])
+    tab = attn.rope_tables(max_pos, d, 1e6, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(iters):
+            fn()
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+
+    ms = inp["max_seqlen"]
+    t_f = timed(lambda: attn.rope(q, k, cu, tab, max_seqlen=ms))
+    t_i = timed(lambda: attn.rope(q, k, cu, tab, max_seqlen=ms, inverse=True))
+    # q and k read and written once, one table row (cos and sin) per token.
+    nbytes = 2 * T * (h_q + h_kv) * d * 2 + T * d * 4
+    out = {"workload": f"{TRAIN_WORKLOAD} q+k ({T} tokens, H_q={h_q}, H_kv={h_kv}, d={d})",
+           "fwd_us": round(t_f * 1e6, 2), "fwd_GB/s": round(nbytes / t_f / 1e9, 1),
+           "inv_us": round(t_i * 1e6, 2), "inv_GB/s": round(nbytes / t_i / 1e9, 1),
+           "fwd_hbm_peak_frac": round(nbytes / t_f / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    qp, kn, vn, cq, kp, vp, bt, ctx = (pre[n].to(dev) for n in (
+        "q", "k_new", "v_new", "cu_q", "k_pool", "v_pool", "block_table", "ctx_lens"))
+    o = torch.empty_like(qp)
+    lse = torch.empty((qp.shape[1], qp.shape[0]), dtype=torch.float32, device=dev)
+    kw = dict(max_ctx_len=pre["max_ctx"], max_q_len=pre["max_q_len"])
+    t_app = timed(lambda: attn.kv_append(kn, vn, cq, bt, ctx, kp, vp, **kw))
+    t_app_r = timed(lambda: attn.kv_append(kn, vn, cq, bt, ctx, kp, vp, rope=tab, **kw))
+    t_att = timed(lambda: attn.prefill_paged(qp, kp, vp, bt, ctx, cq, pre["scale"], o=o, lse=lse,
+                                             **kw))
+    t_att_r = timed(lambda: attn.prefill_paged(qp, kp, vp, bt, ctx, cq, pre["scale"], o=o,
+                                               lse=lse, rope=tab, **kw))
+    out.update({"prefill_workload": "paged_prefill",
+                "append_us": round(t_app * 1e6, 2), "append_rope_us": round(t_app_r * 1e6, 2),
+                "prefill_us": round(t_att * 1e6, 2), "prefill_rope_us": round(t_att_r * 1e6, 2)})
+    return out
 
 
 def norm_bytes(rows, n):
@@ -469,6 +524,7 @@ def main():
     out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
     out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
     out["sampling"] = bench_sampling(attn, W, dev, max(args.steps, 5))
+    out["rope"] = bench_rope(attn, W, dev, max(args.steps, 5))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_budget)
         cb.pop("seconds", None)

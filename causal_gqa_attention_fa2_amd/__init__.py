@@ -9,7 +9,9 @@ thin ctypes wrappers of attn_fwd, attn_bwd, attn_decode_paged,
 attn_kv_append and attn_prefill_paged; the shared library is loaded on first
 use and every call raises if it is missing. ``rmsnorm_fwd`` / ``rmsnorm_bwd``
 wrap attn_rmsnorm_fwd / attn_rmsnorm_bwd, the layer normalisation next to
-attention.
+attention. ``rope_tables`` / ``rope`` wrap attn_rope_tables_init / attn_rope
+(rotary position embedding of q and k, and its inverse); ``kv_append`` and
+``prefill_paged`` take ``rope=(cos, sin)`` to rotate inside those kernels.
 """
 from .attn import (  # noqa: F401
     AttnError,
@@ -27,6 +29,9 @@ from .attn import (  # noqa: F401
     paged_dims,
     prefill_dims,
     prefill_paged,
+    RopeTables,
+    rope,
+    rope_tables,
     rmsnorm_bwd,
     rmsnorm_bwd_workspace_bytes,
     rmsnorm_fwd,

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTE
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
             "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
-            "attn_sample",
+            "attn_sample", "attn_rope_tables_init", "attn_rope", "attn_kv_append_rope",
+            "attn_prefill_paged_rope",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
 
@@ -54,6 +55,10 @@ class PrefillDims(ctypes.Structure):
 
 class SampleDims(ctypes.Structure):
     _fields_ = [("n_rows", ctypes.c_int32), ("vocab", ctypes.c_int32)]
+
+
+class RopeTables(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("max_pos", ctypes.c_int32)]
 
 
 class NormDims(ctypes.Structure):
@@ -111,6 +116,19 @@ def load_library():
     lib.attn_sample.argtypes = [ctypes.POINTER(SampleDims), _vp, _vp, ctypes.c_float,
                                 ctypes.c_int32, ctypes.c_float, _vp, _vp]
     lib.attn_sample.restype = ctypes.c_int
+    lib.attn_rope_tables_init.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _vp,
+                                          _vp, _vp]
+    lib.attn_rope_tables_init.restype = ctypes.c_int
+    lib.attn_rope.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, ctypes.c_int32,
+                              ctypes.POINTER(RopeTables), ctypes.c_int32, _vp]
+    lib.attn_rope.restype = ctypes.c_int
+    lib.attn_kv_append_rope.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.POINTER(RopeTables), _vp, _vp, _vp]
+    lib.attn_kv_append_rope.restype = ctypes.c_int
+    lib.attn_prefill_paged_rope.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp, _vp, _vp,
+                                            _vp, ctypes.POINTER(RopeTables), _vp, _vp,
+                                            ctypes.c_float, _vp]
+    lib.attn_prefill_paged_rope.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -334,8 +352,10 @@ def _prefill_args(k_pool, v_pool, block_table, ctx_lens, cu_q, dev):
 
 
 def kv_append(k_new, v_new, cu_q, block_table, ctx_lens, k_pool, v_pool, max_ctx_len=None,
-              max_q_len=None):
-    """attn_kv_append: writes the new keys/values into k_pool / v_pool in place."""
+              max_q_len=None, rope=None):
+    """attn_kv_append: writes the new keys/values into k_pool / v_pool in place.
+    rope=(cos, sin) (tables from ``rope_tables``) calls attn_kv_append_rope,
+    which rotates the keys by their context positions on the way."""
     lib = load_library()
     dev = k_new.device
     _need(k_new, "k_new", torch.float16, 3)
@@ -348,6 +368,13 @@ def kv_append(k_new, v_new, cu_q, block_table, ctx_lens, k_pool, v_pool, max_ctx
     dims = prefill_dims(k_new, k_pool, block_table, cu_q, max_ctx_len, max_q_len)
     if debug_validate_enabled():
         validate_prefill(dims, cu_q, block_table, ctx_lens)
+    if rope is not None:
+        tab = _rope_struct(rope, d=k_new.shape[2], device=dev)
+        _check("attn_kv_append_rope",
+               lib.attn_kv_append_rope(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cu_q),
+                                       _ptr(block_table), _ptr(ctx_lens), ctypes.byref(tab),
+                                       _ptr(k_pool), _ptr(v_pool), _stream()))
+        return k_pool, v_pool
     _check("attn_kv_append",
            lib.attn_kv_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cu_q),
                               _ptr(block_table), _ptr(ctx_lens), _ptr(k_pool), _ptr(v_pool),
@@ -356,8 +383,10 @@ def kv_append(k_new, v_new, cu_q, block_table, ctx_lens, k_pool, v_pool, max_ctx
 
 
 def prefill_paged(q, k_pool, v_pool, block_table, ctx_lens, cu_q, scale=None, o=None, lse=None,
-                  with_lse=True, max_ctx_len=None, max_q_len=None):
-    """attn_prefill_paged: returns (o fp16 [total_q, h_q, d], lse fp32 [h_q, total_q] or None)."""
+                  with_lse=True, max_ctx_len=None, max_q_len=None, rope=None):
+    """attn_prefill_paged: returns (o fp16 [total_q, h_q, d], lse fp32 [h_q, total_q] or None).
+    rope=(cos, sin) calls attn_prefill_paged_rope, which rotates the queries
+    by their context positions as it loads them (q is not modified)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.float16, 3)
@@ -382,11 +411,76 @@ def prefill_paged(q, k_pool, v_pool, block_table, ctx_lens, cu_q, scale=None, o=
     dims = prefill_dims(q, k_pool, block_table, cu_q, max_ctx_len, max_q_len)
     if debug_validate_enabled():
         validate_prefill(dims, cu_q, block_table, ctx_lens)
+    if rope is not None:
+        tab = _rope_struct(rope, d=d, device=dev)
+        _check("attn_prefill_paged_rope",
+               lib.attn_prefill_paged_rope(ctypes.byref(dims), _ptr(q), _ptr(k_pool),
+                                           _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens),
+                                           _ptr(cu_q), ctypes.byref(tab), _ptr(o), _ptr(lse),
+                                           float(scale), _stream()))
+        return o, lse
     _check("attn_prefill_paged",
            lib.attn_prefill_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                   _ptr(block_table), _ptr(ctx_lens), _ptr(cu_q), _ptr(o),
                                   _ptr(lse), float(scale), _stream()))
     return o, lse
+
+
+def _rope_struct(rope, d, device):
+    cos, sin = rope
+    _need(cos, "rope cos", torch.float32, 2, device)
+    _need(sin, "rope sin", torch.float32, 2, device)
+    if cos.shape != sin.shape or cos.shape[1] != d // 2:
+        raise ValueError("rope tables must both be [max_pos, head_dim / 2]")
+    return RopeTables(cos.data_ptr(), sin.data_ptr(), cos.shape[0])
+
+
+def rope_tables(max_pos, head_dim, base=1e6, device="cuda"):
+    """attn_rope_tables_init: (cos, sin) fp32 [max_pos, head_dim / 2] of the
+    angles p * base^(-2j / head_dim), evaluated on the device in fp64."""
+    lib = load_library()
+    cos = torch.empty((max_pos, head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check("attn_rope_tables_init",
+           lib.attn_rope_tables_init(int(max_pos), int(head_dim), float(base), _ptr(cos),
+                                     _ptr(sin), _stream()))
+    return cos, sin
+
+
+def rope(q, k, cu_seqlens, tables, ctx_lens=None, max_ctx_len=None, max_seqlen=None,
+         inverse=False):
+    """attn_rope: rotates q [T, h_q, d] and k [T, h_kv, d] in place (either may
+    be None) by their positions within their sequences, or, with ctx_lens,
+    by their context positions as the new chunk of a cached sequence.
+    inverse=True applies the transposed rotation (the backward of dq, dk)."""
+    lib = load_library()
+    ref = q if q is not None else k
+    if ref is None:
+        raise ValueError("nothing to rotate")
+    dev = ref.device
+    if q is not None:
+        _need(q, "q", torch.float16, 3)
+    if k is not None:
+        _need(k, "k", torch.float16, 3, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    T, d = ref.shape[0], ref.shape[2]
+    h_q = q.shape[1] if q is not None else k.shape[1]
+    h_kv = k.shape[1] if k is not None else h_q
+    if (q is not None and k is not None) and (q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]):
+        raise ValueError("q and k disagree on tokens or head_dim")
+    if max_seqlen is None:  # host copy: synchronises, meant for tests
+        c = cu_seqlens.cpu()
+        max_seqlen = int((c[1:] - c[:-1]).max()) if c.numel() > 1 else 0
+    if ctx_lens is not None:
+        _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+        if max_ctx_len is None:  # host copy: synchronises, meant for tests
+            max_ctx_len = int(ctx_lens.max()) if ctx_lens.numel() else 0
+    dims = VarlenDims(cu_seqlens.numel() - 1, T, max_seqlen, h_q, h_kv, d)
+    tab = _rope_struct(tables, d=d, device=dev)
+    _check("attn_rope",
+           lib.attn_rope(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(cu_seqlens), _ptr(ctx_lens),
+                         int(max_ctx_len or 0), ctypes.byref(tab), int(bool(inverse)), _stream()))
+    return q, k
 
 
 def check_prefill_host(dims, cu_host, block_table_host, ctx_host):

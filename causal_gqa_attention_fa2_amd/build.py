@@ -22,7 +22,7 @@ PROBE_SOURCE = "probe_peaks.hip"
 PROBE_LIB_PATH = os.path.join(PKG, "libattn_probe.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
-           "attn_norm.hip", "attn_sample.hip"]
+           "attn_norm.hip", "attn_sample.hip", "attn_rope.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Per-source extra flags. The forward kernel never produces or consumes NaN on

@@ -127,6 +127,15 @@ size_t norm_ws_bytes(const attn_norm_dims* d) {
   return align_up((size_t)cgqa::rmsnorm_bwd_num_wgs(d->rows, d->n) * d->n * sizeof(float));
 }
 
+// RoPE tables of a call: both present, 16-byte aligned, max_pos >= 1 and
+// covering every position the call can form (max_positions of them).
+attn_status check_rope(const attn_rope_tables* t, int64_t max_positions) {
+  if (!t || !t->cos || !t->sin || t->max_pos <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(t->cos) || !aligned16(t->sin)) return ATTN_ERR_INVALID_ARG;
+  if (max_positions > t->max_pos) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,12 +270,15 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
   return cgqa::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-attn_status attn_kv_append(const attn_prefill_dims* dims, const void* k_new, const void* v_new,
-                           const int32_t* cu_q, const int32_t* block_table,
-                           const int32_t* ctx_lens, void* k_pool, void* v_pool, void* stream) {
+static attn_status kv_append_impl(const attn_prefill_dims* dims, const void* k_new,
+                                  const void* v_new, const int32_t* cu_q,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  const attn_rope_tables* rope, void* k_pool, void* v_pool,
+                                  void* stream) {
   bool empty = false;
   attn_status st = check_prefill(dims, &empty);
   if (st != ATTN_OK) return st;
+  if (rope && (st = check_rope(rope, dims->paged.max_ctx_len)) != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   if (!k_new || !v_new || !cu_q || !block_table || !ctx_lens || !k_pool || !v_pool)
     return ATTN_ERR_INVALID_ARG;
@@ -288,16 +300,40 @@ attn_status attn_kv_append(const attn_prefill_dims* dims, const void* k_new, con
   a.max_blocks_per_seq = dims->paged.max_blocks_per_seq;
   a.num_blocks = dims->paged.num_blocks;
   a.max_ctx_len = dims->paged.max_ctx_len;
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.rope_max_pos = rope->max_pos;
+  }
   return cgqa::launch_kv_append(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, const void* k_pool,
-                               const void* v_pool, const int32_t* block_table,
-                               const int32_t* ctx_lens, const int32_t* cu_q, void* o,
-                               float* lse, float scale, void* stream) {
+attn_status attn_kv_append(const attn_prefill_dims* dims, const void* k_new, const void* v_new,
+                           const int32_t* cu_q, const int32_t* block_table,
+                           const int32_t* ctx_lens, void* k_pool, void* v_pool, void* stream) {
+  return kv_append_impl(dims, k_new, v_new, cu_q, block_table, ctx_lens, nullptr, k_pool, v_pool,
+                        stream);
+}
+
+attn_status attn_kv_append_rope(const attn_prefill_dims* dims, const void* k_new,
+                                const void* v_new, const int32_t* cu_q,
+                                const int32_t* block_table, const int32_t* ctx_lens,
+                                const attn_rope_tables* rope, void* k_pool, void* v_pool,
+                                void* stream) {
+  if (!rope) return ATTN_ERR_INVALID_ARG;
+  return kv_append_impl(dims, k_new, v_new, cu_q, block_table, ctx_lens, rope, k_pool, v_pool,
+                        stream);
+}
+
+static attn_status prefill_impl(const attn_prefill_dims* dims, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* ctx_lens, const int32_t* cu_q,
+                                const attn_rope_tables* rope, void* o, float* lse, float scale,
+                                void* stream) {
   bool empty = false;
   attn_status st = check_prefill(dims, &empty);
   if (st != ATTN_OK) return st;
+  if (rope && (st = check_rope(rope, dims->paged.max_ctx_len)) != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !cu_q || !o)
     return ATTN_ERR_INVALID_ARG;
@@ -317,6 +353,11 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
   a.max_blocks_per_seq = dims->paged.max_blocks_per_seq;
   a.num_blocks = dims->paged.num_blocks;
   a.max_ctx_len = dims->paged.max_ctx_len;
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.rope_max_pos = rope->max_pos;
+  }
   a.n_seqs = dims->paged.n_seqs;
   a.total_tokens = dims->total_q;
   a.max_seqlen = dims->max_q_len;
@@ -325,6 +366,68 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
   a.head_dim = dims->paged.head_dim;
   a.scale = scale;
   return cgqa::launch_prefill(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* ctx_lens, const int32_t* cu_q, void* o,
+                               float* lse, float scale, void* stream) {
+  return prefill_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, cu_q, nullptr, o, lse, scale,
+                      stream);
+}
+
+attn_status attn_prefill_paged_rope(const attn_prefill_dims* dims, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const int32_t* cu_q, const attn_rope_tables* rope, void* o,
+                                    float* lse, float scale, void* stream) {
+  if (!rope) return ATTN_ERR_INVALID_ARG;
+  return prefill_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, cu_q, rope, o, lse, scale,
+                      stream);
+}
+
+attn_status attn_rope_tables_init(int32_t max_pos, int32_t head_dim, double base, float* cos_t,
+                                  float* sin_t, void* stream) {
+  if (max_pos <= 0 || !(base > 1.0) || !cos_t || !sin_t) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(cos_t) || !aligned16(sin_t)) return ATTN_ERR_INVALID_ARG;
+  cgqa::RopeTableArgs a;
+  a.cos = cos_t;
+  a.sin = sin_t;
+  a.max_pos = max_pos;
+  a.head_dim = head_dim;
+  a.base = base;
+  return cgqa::launch_rope_tables(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_rope(const attn_varlen_dims* dims, void* q, void* k, const int32_t* cu_seqlens,
+                      const int32_t* ctx_lens, int32_t max_ctx_len, const attn_rope_tables* rope,
+                      int32_t inverse, void* stream) {
+  bool empty = false;
+  attn_status st = check_varlen(dims, &empty);
+  if (st != ATTN_OK) return st;
+  if (dims->n_seqs > 65535) return ATTN_ERR_UNSUPPORTED;  // grid y limit
+  if (ctx_lens && max_ctx_len < dims->max_seqlen) return ATTN_ERR_INVALID_ARG;
+  if ((st = check_rope(rope, ctx_lens ? max_ctx_len : dims->max_seqlen)) != ATTN_OK) return st;
+  if (empty || (!q && !k)) return ATTN_OK;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u) || ((uintptr_t)ctx_lens & 3u) ||
+      !aligned16(q) || !aligned16(k))
+    return ATTN_ERR_INVALID_ARG;
+  cgqa::RopeArgs a;
+  a.q = q;
+  a.k = k;
+  a.cu_seqlens = cu_seqlens;
+  a.ctx_lens = ctx_lens;
+  a.cos = rope->cos;
+  a.sin = rope->sin;
+  a.max_pos = rope->max_pos;
+  a.n_seqs = dims->n_seqs;
+  a.max_seqlen = dims->max_seqlen;
+  a.h_q = dims->h_q;
+  a.h_kv = dims->h_kv;
+  a.head_dim = dims->head_dim;
+  a.inverse = inverse != 0;
+  return cgqa::launch_rope(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_check_prefill(const attn_prefill_dims* dims, const int32_t* cu,

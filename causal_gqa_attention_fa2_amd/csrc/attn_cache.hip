@@ -7,9 +7,11 @@
 // tokens are the last L_b of its ctx[b] positions) and goes to slot t % 16
 // of pool block bt[b][t / 16]. Pure data movement, bound by HBM: each
 // work-group moves 16 tokens of one sequence in 16-byte pieces, every byte
-// read once and written once.
-#include <hip/hip_runtime.h>
-
+// read once and written once. The variant with RoPE tables rotates each key
+// by its position t on the way (rope_pair in cdna4.h: the same bits as the
+// standalone RoPE pass); a thread then holds the two 16-byte pieces whose
+// dimensions pair up (8p .. 8p+7 and d/2 + 8p ..).
+#include "cdna4.h"
 #include "kernels.h"
 
 namespace cgqa {
@@ -26,10 +28,14 @@ struct AppendParams {
   const int32_t* __restrict__ ctx;
   uint4* __restrict__ k_pool;
   uint4* __restrict__ v_pool;
+  const float* __restrict__ cos_t;  // RoPE tables [max_pos, d / 2] (ROPE only)
+  const float* __restrict__ sin_t;
+  int max_pos;
   int cpt;  // 16-byte pieces per token row (h_kv * d / 8)
   int max_blocks, num_blocks, max_ctx;
 };
 
+template <int D, bool ROPE>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.y;
   const int s0 = p.cu[b];
@@ -50,11 +56,35 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   __syncthreads();
   const int n = ntok * p.cpt;
   const size_t src0 = (size_t)(s0 + i0) * p.cpt;  // the tokens' rows are contiguous
-  for (int e = threadIdx.x; e < n; e += kAppendThreads) {
-    const int tok = e / p.cpt;
-    const size_t dst = dst_row[tok] + (e - tok * p.cpt);
-    p.k_pool[dst] = p.k_new[src0 + e];
-    p.v_pool[dst] = p.v_new[src0 + e];
+  if constexpr (ROPE) {
+    constexpr int PP = D / 16;  // pieces per half head
+    const int per_tok = p.cpt / 2;  // pairs of pieces per token
+    for (int e = threadIdx.x; e < ntok * per_tok; e += kAppendThreads) {
+      const int tok = e / per_tok;
+      const int r = e - tok * per_tok;
+      const int h = r / PP;
+      const int pc = r - h * PP;
+      const int pos = min(off + i0 + tok, p.max_pos - 1);
+      const int piece = tok * p.cpt + h * 2 * PP + pc;  // low piece; high one PP further
+      f16x8 lo = __builtin_bit_cast(f16x8, p.k_new[src0 + piece]);
+      f16x8 hi = __builtin_bit_cast(f16x8, p.k_new[src0 + piece + PP]);
+      rope_rotate8(lo, hi, p.cos_t + (size_t)pos * (D / 2) + 8 * pc,
+                   p.sin_t + (size_t)pos * (D / 2) + 8 * pc, 1.f);
+      const size_t dst = dst_row[tok] + (piece - tok * p.cpt);
+      p.k_pool[dst] = __builtin_bit_cast(uint4, lo);
+      p.k_pool[dst + PP] = __builtin_bit_cast(uint4, hi);
+    }
+    for (int e = threadIdx.x; e < n; e += kAppendThreads) {
+      const int tok = e / p.cpt;
+      p.v_pool[dst_row[tok] + (e - tok * p.cpt)] = p.v_new[src0 + e];
+    }
+  } else {
+    for (int e = threadIdx.x; e < n; e += kAppendThreads) {
+      const int tok = e / p.cpt;
+      const size_t dst = dst_row[tok] + (e - tok * p.cpt);
+      p.k_pool[dst] = p.k_new[src0 + e];
+      p.v_pool[dst] = p.v_new[src0 + e];
+    }
   }
 }
 
@@ -69,12 +99,20 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   p.ctx = a.ctx_lens;
   p.k_pool = (uint4*)a.k_pool;
   p.v_pool = (uint4*)a.v_pool;
+  p.cos_t = a.rope_cos;
+  p.sin_t = a.rope_sin;
+  p.max_pos = a.rope_max_pos;
   p.cpt = a.h_kv * a.head_dim / 8;
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
   p.max_ctx = a.max_ctx_len;
   const dim3 grid((a.max_new + kTokPerWG - 1) / kTokPerWG, a.n_seqs);
-  hipLaunchKernelGGL(kv_append_kernel, grid, dim3(kAppendThreads), 0, stream, p);
+  if (a.rope_cos == nullptr)
+    hipLaunchKernelGGL((kv_append_kernel<128, false>), grid, dim3(kAppendThreads), 0, stream, p);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((kv_append_kernel<128, true>), grid, dim3(kAppendThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kv_append_kernel<64, true>), grid, dim3(kAppendThreads), 0, stream, p);
   return hipGetLastError();
 }
 

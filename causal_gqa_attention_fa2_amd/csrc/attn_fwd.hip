@@ -61,6 +61,10 @@ struct FwdParams {
   const int32_t* __restrict__ bt;
   const int32_t* __restrict__ ctx;
   int max_blocks, num_blocks, max_ctx;
+  // Paged prefill with RoPE only: cos / sin tables [max_pos, D / 2].
+  const float* __restrict__ cos_t;
+  const float* __restrict__ sin_t;
+  int max_pos;
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles;
   float scale_log2;  // scale * log2(e)
 };
@@ -71,8 +75,11 @@ struct FwdParams {
 // sequence b (rows cu[b] .. cu[b+1]-1 of q) are the last L_b of its ctx[b]
 // context positions, so query i sits at position ctx[b] - L_b + i; the keys
 // and values of position t are slot t % 16 of pool block bt[b][t / 16].
-template <int D, bool PAGED>
+// ROPE (paged only): the queries are rotated by their context positions as
+// they are loaded (the keys were rotated when they were appended).
+template <int D, bool PAGED, bool ROPE = false>
 __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
+  static_assert(PAGED || !ROPE, "query rotation is a prefill option");
   constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
   constexpr int CH = D / 8;    // 16-byte chunks per row
@@ -167,6 +174,15 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
 #pragma unroll
     for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
+  }
+  if constexpr (ROPE) {
+    // Dimension 16t + 8hi + e (t < NT/2) pairs with the one D/2 further,
+    // which is element e of fragment t + NT/2 of the same lane.
+    const int pos = min(off + min(qpos, L - 1), p.max_pos - 1);
+    const float* ct = p.cos_t + (size_t)pos * (D / 2) + 8 * hi;
+    const float* st = p.sin_t + (size_t)pos * (D / 2) + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < NT / 2; ++t) rope_rotate8(qf[t], qf[t + NT / 2], ct + 16 * t, st + 16 * t, 1.f);
   }
 
   f32x16 oacc[ND];
@@ -340,6 +356,9 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
   p.max_ctx = a.max_ctx_len;
+  p.cos_t = a.rope_cos;
+  p.sin_t = a.rope_sin;
+  p.max_pos = a.rope_max_pos;
   p.n_seqs = a.n_seqs;
   p.T = a.total_tokens;
   p.h_q = a.h_q;
@@ -353,10 +372,16 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   p.n_qtiles = (a.max_seqlen + BR - 1) / BR;
   p.scale_log2 = a.scale * kLog2e;
   const dim3 grid(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
-  if (a.head_dim == 128)
+  if (PAGED && a.rope_cos != nullptr) {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((fwd_kernel<128, true, true>), grid, dim3(kNTH), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<64, true, true>), grid, dim3(kNTH), 0, stream, p);
+  } else if (a.head_dim == 128) {
     hipLaunchKernelGGL((fwd_kernel<128, PAGED>), grid, dim3(kNTH), 0, stream, p);
-  else
+  } else {
     hipLaunchKernelGGL((fwd_kernel<64, PAGED>), grid, dim3(kNTH), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

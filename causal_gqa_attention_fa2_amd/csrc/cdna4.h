@@ -170,4 +170,50 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
   return z;
 }
 
+// fp64 -> fp16 with a single correct rounding (to nearest even): the value is
+// first narrowed to fp32 with round-to-odd (truncate, then set the last bit if
+// anything was dropped), which keeps enough information for the final
+// fp32 -> fp16 rounding to equal a direct one. (A plain fp64 -> fp32 -> fp16
+// chain rounds twice and is off by one unit now and then.)
+__device__ __forceinline__ f16 f64_to_f16_rn(double y) {
+  float t = (float)y;
+  if ((double)t != y) {
+    uint32_t u = __builtin_bit_cast(uint32_t, t);
+    if (__builtin_fabs((double)t) > __builtin_fabs(y)) u -= 1u;  // toward zero
+    t = __builtin_bit_cast(float, u | 1u);
+  }
+  return (f16)t;
+}
+
+// Rotary position embedding of one dimension pair (a = dimension j, b =
+// dimension j + d/2) by the angle whose cosine and sine are c and s (fp32
+// table values; pass -s for the inverse rotation):
+//   a' = a c - b s,   b' = b c + a s.
+// Products of an fp16 and an fp32 value are exact in fp64 and each fma rounds
+// once, so a' and b' are the fp64 values of the formula, rounded once more to
+// fp16 by f64_to_f16_rn.
+__device__ __forceinline__ void rope_pair(f16& a, f16& b, float c, float s) {
+  const double x1 = (double)a, x2 = (double)b, cd = (double)c, sd = (double)s;
+  const double y1 = __builtin_fma(x1, cd, -(x2 * sd));
+  const double y2 = __builtin_fma(x2, cd, x1 * sd);
+  a = f64_to_f16_rn(y1);
+  b = f64_to_f16_rn(y2);
+}
+
+// rope_pair on the 8 pairs (lo[e], hi[e]), e = 0..7, with the table entries
+// c[e], s[e] (8 consecutive fp32 values, 16-byte aligned); sgn = -1 turns
+// the other way (the inverse rotation).
+__device__ __forceinline__ void rope_rotate8(f16x8& lo, f16x8& hi, const float* c,
+                                             const float* s, float sgn) {
+  const f32x4 c0 = ((const f32x4*)c)[0], c1 = ((const f32x4*)c)[1];
+  const f32x4 s0 = ((const f32x4*)s)[0], s1 = ((const f32x4*)s)[1];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f16 a = lo[e], b = hi[e];
+    rope_pair(a, b, e < 4 ? c0[e & 3] : c1[e & 3], sgn * (e < 4 ? s0[e & 3] : s1[e & 3]));
+    lo[e] = a;
+    hi[e] = b;
+  }
+}
+
 }  // namespace cgqa

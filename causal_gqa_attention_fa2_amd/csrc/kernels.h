@@ -22,6 +22,11 @@ struct FwdArgs {
   const int32_t* block_table = nullptr;
   const int32_t* ctx_lens = nullptr;
   int max_blocks_per_seq = 0, num_blocks = 0, max_ctx_len = 0;
+  // Paged prefill only: RoPE tables [rope_max_pos, head_dim / 2] to rotate the
+  // queries with as they are loaded, or null.
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int rope_max_pos = 0;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   float scale;
 };
@@ -35,7 +40,34 @@ struct AppendArgs {
   const int32_t* ctx_lens;
   void* k_pool;
   void* v_pool;
+  // RoPE tables [rope_max_pos, head_dim / 2] to rotate the keys with on their
+  // way into the pool, or null.
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int rope_max_pos = 0;
   int n_seqs, max_new, h_kv, head_dim, max_blocks_per_seq, num_blocks, max_ctx_len;
+};
+
+// RoPE tables: cos / sin fp32 [max_pos, head_dim / 2].
+struct RopeTableArgs {
+  float* cos;
+  float* sin;
+  int max_pos, head_dim;
+  double base;
+};
+
+// In-place RoPE of packed q [T, h_q, d] and k [T, h_kv, d] (either may be
+// null). Positions: index within the sequence, or ctx_lens[b] - L_b + i.
+struct RopeArgs {
+  void* q;
+  void* k;
+  const int32_t* cu_seqlens;
+  const int32_t* ctx_lens;  // may be null
+  const float* cos;
+  const float* sin;
+  int max_pos;
+  int n_seqs, max_seqlen, h_q, h_kv, head_dim;
+  bool inverse;
 };
 
 struct BwdArgs {
@@ -129,6 +161,8 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_rope_tables(const RopeTableArgs& a, hipStream_t stream);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // dS blocks of the backward's dS path: one 32 x 32 fp16 block (2 KiB) per
 // (sequence, query head, 32-row query block, 32-key block), indexed with the

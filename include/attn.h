@@ -221,6 +221,75 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
                                const int32_t* ctx_lens, const int32_t* cu_q, void* o,
                                float* lse, float scale, void* stream);
 
+/*
+ * Rotary position embedding (RoPE) -- the rotation of queries and keys that
+ * comes right before attention (the mlllm.io article, "What happened", lists
+ * RoPE among the hand-written kernels). The pages print no formula; the
+ * library uses the rotate-half pairing of Qwen3, the model the pages
+ * benchmark: dimension j < d/2 of every head turns together with dimension
+ * j + d/2 by the angle pos * theta_j,
+ *   x'_j = x_j cos - x_{j+d/2} sin,   x'_{j+d/2} = x_{j+d/2} cos + x_j sin,
+ * with cos / sin read from caller-owned fp32 tables [max_pos, d/2] (device
+ * pointers, 16-byte aligned; row p holds position p). Every kernel rotates
+ * in fp64 and rounds once to fp16, so the rotated values are the same bits
+ * whichever entry point rotates them.
+ */
+typedef struct attn_rope_tables {
+    const float* cos;
+    const float* sin;
+    int32_t max_pos;
+} attn_rope_tables;
+
+/*
+ * attn_rope_tables_init -- fill cos / sin fp32 [max_pos, head_dim/2] with
+ * cos(p * base^(-2j/head_dim)) and sin(...), evaluated in fp64 and rounded
+ * to fp32. head_dim 64 or 128, base > 1 (Qwen3: 1e6), max_pos >= 1.
+ */
+attn_status attn_rope_tables_init(int32_t max_pos, int32_t head_dim, double base, float* cos,
+                                  float* sin, void* stream);
+
+/*
+ * attn_rope -- rotate packed q [total_tokens, h_q, d] and k [total_tokens,
+ * h_kv, d] (fp16, in place; either may be NULL) by their positions.
+ *   ctx_lens == NULL: token i of a sequence (rows cu_seqlens[b] + i) is at
+ *     position i (training over packed sequences; max_pos >= max_seqlen).
+ *   ctx_lens != NULL: the tokens are the new chunk of a cached sequence, at
+ *     positions ctx_lens[b] - L_b + i (max_ctx_len bounds ctx_lens; max_pos
+ *     >= max_ctx_len); a sequence whose L_b exceeds its context is skipped.
+ *   inverse != 0 applies the transposed rotation: the backward, which turns
+ *     dq and dk of the rotated tensors into those of the unrotated ones.
+ * Positions beyond the tables are clamped to max_pos - 1 (only reachable
+ * with invalid ctx_lens). Bitwise deterministic.
+ */
+attn_status attn_rope(const attn_varlen_dims* dims, void* q, void* k, const int32_t* cu_seqlens,
+                      const int32_t* ctx_lens, int32_t max_ctx_len, const attn_rope_tables* rope,
+                      int32_t inverse, void* stream);
+
+/*
+ * attn_kv_append_rope -- attn_kv_append that rotates each new key by its
+ * context position on its way into the pool (values are copied as they
+ * are). The pool then holds the same bits as attn_rope on k_new (with
+ * ctx_lens) followed by attn_kv_append. rope->max_pos >= max_ctx_len.
+ */
+attn_status attn_kv_append_rope(const attn_prefill_dims* dims, const void* k_new,
+                                const void* v_new, const int32_t* cu_q,
+                                const int32_t* block_table, const int32_t* ctx_lens,
+                                const attn_rope_tables* rope, void* k_pool, void* v_pool,
+                                void* stream);
+
+/*
+ * attn_prefill_paged_rope -- attn_prefill_paged whose queries are rotated by
+ * their context positions as they are loaded (q itself is not modified);
+ * the keys in the pool are taken as already rotated (attn_kv_append_rope).
+ * O and LSE are bitwise those of attn_rope on q followed by
+ * attn_prefill_paged. rope->max_pos >= max_ctx_len.
+ */
+attn_status attn_prefill_paged_rope(const attn_prefill_dims* dims, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* ctx_lens,
+                                    const int32_t* cu_q, const attn_rope_tables* rope, void* o,
+                                    float* lse, float scale, void* stream);
+
 /* Shape of an RMSNorm call: `rows` rows of `n` values (n % 8 == 0,
  * 8 <= n <= 2048; rows >= 0). */
 typedef struct attn_norm_dims {

@@ -290,3 +290,58 @@ def test_sample_argument_checks(lib):
     assert call(d, lg=0) == INVALID
     assert call(d, out=FAKE + 2) == INVALID
     assert call(SampleDims(0, 1000), lg=0, u=0, out=0) == OK
+
+
+def test_rope_argument_checks(lib):
+    """attn_rope_tables_init / attn_rope / attn_kv_append_rope /
+    attn_prefill_paged_rope reject bad tables, shapes and pointers before any
+    HIP call; empty batches are no-ops."""
+    from causal_gqa_attention_fa2_amd.attn import PrefillDims, RopeTables
+    p = ctypes.c_void_p
+    init = lib.attn_rope_tables_init
+    assert init(0, 128, 1e6, p(FAKE), p(FAKE), None) == INVALID
+    assert init(100, 96, 1e6, p(FAKE), p(FAKE), None) == UNSUPPORTED
+    assert init(100, 128, 1.0, p(FAKE), p(FAKE), None) == INVALID
+    assert init(100, 128, 1e6, None, p(FAKE), None) == INVALID
+    assert init(100, 128, 1e6, p(FAKE), p(FAKE + 4), None) == INVALID
+
+    def tab(mp=4096, c=FAKE, s=FAKE):
+        return ctypes.byref(RopeTables(c, s, mp))
+
+    def vd(n=2, T=100, mx=60, h_q=16, h_kv=8, d=128):
+        return ctypes.byref(VarlenDims(n, T, mx, h_q, h_kv, d))
+
+    def rope(dm=None, q=FAKE, k=FAKE, cu=FAKE, ctx=None, mctx=0, t=None, inv=0):
+        return lib.attn_rope(dm if dm is not None else vd(), p(q), p(k), p(cu), p(ctx), mctx,
+                             t if t is not None else tab(), inv, None)
+
+    assert lib.attn_rope(vd(), p(FAKE), p(FAKE), p(FAKE), None, 0, None, 0, None) == INVALID
+    assert rope(t=tab(mp=59)) == INVALID            # tables shorter than max_seqlen
+    assert rope(t=tab(mp=0)) == INVALID
+    assert rope(t=tab(c=0)) == INVALID
+    assert rope(t=tab(s=FAKE + 8)) == INVALID       # misaligned table
+    assert rope(ctx=FAKE, mctx=50) == INVALID       # max_ctx_len below max_seqlen
+    assert rope(ctx=FAKE, mctx=5000) == INVALID     # contexts past the tables
+    assert rope(dm=vd(d=96)) == UNSUPPORTED
+    assert rope(dm=vd(h_q=12)) == INVALID
+    assert rope(q=FAKE + 2) == INVALID
+    assert rope(cu=FAKE + 2) == INVALID
+    assert rope(dm=vd(n=0, T=0, mx=0)) == OK        # empty batch
+    assert rope(q=0, k=0) == OK                     # nothing to rotate
+
+    def dims(n=4, max_ctx=1024, tq=300, mq=100):
+        return PrefillDims(PagedDims(n, 16, 8, 128, 16, 64, 1000, max_ctx), tq, mq)
+
+    def app(dm, t):
+        return lib.attn_kv_append_rope(ctypes.byref(dm), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                       p(FAKE), t, p(FAKE), p(FAKE), None)
+
+    def pre(dm, t):
+        return lib.attn_prefill_paged_rope(ctypes.byref(dm), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                           p(FAKE), p(FAKE), t, p(FAKE), p(FAKE), 0.1, None)
+
+    for fn in (app, pre):
+        assert fn(dims(), None) == INVALID
+        assert fn(dims(), tab(mp=1000)) == INVALID  # tables shorter than max_ctx_len
+        assert fn(dims(), tab(c=FAKE + 4)) == INVALID
+        assert fn(dims(n=0, tq=0, mq=0), tab()) == OK
