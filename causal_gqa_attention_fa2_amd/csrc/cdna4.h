@@ -170,17 +170,23 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
   return z;
 }
 
-// fp64 -> fp16 with a single correct rounding (to nearest even): the value is
-// first narrowed to fp32 with round-to-odd (truncate, then set the last bit if
-// anything was dropped), which keeps enough information for the final
-// fp32 -> fp16 rounding to equal a direct one. (A plain fp64 -> fp32 -> fp16
-// chain rounds twice and is off by one unit now and then.)
+// fp64 -> fp16 with a single correct rounding (to nearest even). The value
+// is first rounded to fp32; fp16 midpoints are fp32 numbers, so that step
+// never moves it across one, and fp32 -> fp16 then rounds correctly unless
+// it landed exactly on a midpoint it was not on before (the tie would be
+// broken to even instead of by the discarded part). Only then (and in the
+// fp16 subnormal range, where the test below does not apply) is the fp32
+// value redone with round-to-odd (truncate, set the last bit if anything
+// was dropped), after which the fp32 -> fp16 rounding equals a direct one.
 __device__ __forceinline__ f16 f64_to_f16_rn(double y) {
   float t = (float)y;
-  if ((double)t != y) {
-    uint32_t u = __builtin_bit_cast(uint32_t, t);
-    if (__builtin_fabs((double)t) > __builtin_fabs(y)) u -= 1u;  // toward zero
-    t = __builtin_bit_cast(float, u | 1u);
+  const uint32_t u = __builtin_bit_cast(uint32_t, t) & 0x7fffffffu;
+  if ((u & 0x1fffu) == 0x1000u || u < 0x38800000u) {  // midpoint, or |t| < 2^-14
+    if ((double)t != y) {
+      uint32_t b = __builtin_bit_cast(uint32_t, t);
+      if (__builtin_fabs((double)t) > __builtin_fabs(y)) b -= 1u;  // toward zero
+      t = __builtin_bit_cast(float, b | 1u);
+    }
   }
   return (f16)t;
 }
