@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kRopeTok = 16;  // tokens of one sequence per work-group
 constexpr int kRopeThreads = 256;
+constexpr int kRopeUnroll = 4;  // work items in flight per thread
 
 __global__ __launch_bounds__(kRopeThreads) void rope_tables_kernel(float* __restrict__ cos_t,
                                                                    float* __restrict__ sin_t,
@@ -78,19 +79,41 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeParams p) {
   }
   const int ntok = min(kRopeTok, L - i0);
   const int per_tok = H * PP;
-  for (int e = threadIdx.x; e < ntok * per_tok; e += kRopeThreads) {
-    const int tok = e / per_tok;
-    const int r = e - tok * per_tok;
-    const int h = r / PP;
-    const int pc = r - h * PP;
-    const int pos = min(off + i0 + tok, p.max_pos - 1);
-    f16* row = x + ((size_t)(s0 + i0 + tok) * H + h) * D + 8 * pc;
-    f16x8 lo = *(const f16x8*)row;
-    f16x8 hi = *(const f16x8*)(row + D / 2);
-    rope_rotate8(lo, hi, p.cos_t + (size_t)pos * (D / 2) + 8 * pc,
-                 p.sin_t + (size_t)pos * (D / 2) + 8 * pc, p.sign);
-    *(f16x8*)row = lo;
-    *(f16x8*)(row + D / 2) = hi;
+  const int n = ntok * per_tok;
+  // kRopeUnroll items per thread per pass: all their loads (data and table)
+  // are issued before the first rotation. Items past n repeat item `base`
+  // (always valid) and are not stored.
+  for (int base = threadIdx.x; base < n; base += kRopeThreads * kRopeUnroll) {
+    f16* row[kRopeUnroll];
+    f16x8 lo[kRopeUnroll], hi[kRopeUnroll];
+    f32x4 c0[kRopeUnroll], c1[kRopeUnroll], sn0[kRopeUnroll], sn1[kRopeUnroll];
+#pragma unroll
+    for (int u = 0; u < kRopeUnroll; ++u) {
+      const int e0 = base + u * kRopeThreads;
+      const int e = e0 < n ? e0 : base;
+      const int tok = e / per_tok;
+      const int r = e - tok * per_tok;
+      const int h = r / PP;
+      const int pc = r - h * PP;
+      const int pos = min(off + i0 + tok, p.max_pos - 1);
+      row[u] = x + ((size_t)(s0 + i0 + tok) * H + h) * D + 8 * pc;
+      lo[u] = *(const f16x8*)row[u];
+      hi[u] = *(const f16x8*)(row[u] + D / 2);
+      const f32x4* ct = (const f32x4*)(p.cos_t + (size_t)pos * (D / 2) + 8 * pc);
+      const f32x4* st = (const f32x4*)(p.sin_t + (size_t)pos * (D / 2) + 8 * pc);
+      c0[u] = ct[0];
+      c1[u] = ct[1];
+      sn0[u] = st[0];
+      sn1[u] = st[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kRopeUnroll; ++u) {
+      rope_rotate8(lo[u], hi[u], c0[u], c1[u], sn0[u], sn1[u], p.sign);
+      if (base + u * kRopeThreads < n) {
+        *(f16x8*)row[u] = lo[u];
+        *(f16x8*)(row[u] + D / 2) = hi[u];
+      }
+    }
   }
 }
 

@@ -206,13 +206,11 @@ __device__ __forceinline__ void rope_pair(f16& a, f16& b, float c, float s) {
   b = f64_to_f16_rn(y2);
 }
 
-// rope_pair on the 8 pairs (lo[e], hi[e]), e = 0..7, with the table entries
-// c[e], s[e] (8 consecutive fp32 values, 16-byte aligned); sgn = -1 turns
-// the other way (the inverse rotation).
-__device__ __forceinline__ void rope_rotate8(f16x8& lo, f16x8& hi, const float* c,
-                                             const float* s, float sgn) {
-  const f32x4 c0 = ((const f32x4*)c)[0], c1 = ((const f32x4*)c)[1];
-  const f32x4 s0 = ((const f32x4*)s)[0], s1 = ((const f32x4*)s)[1];
+// rope_pair on the 8 pairs (lo[e], hi[e]), e = 0..7, with cosines c0, c1 and
+// sines s0, s1 (elements 0-3 and 4-7); sgn = -1 turns the other way (the
+// inverse rotation).
+__device__ __forceinline__ void rope_rotate8(f16x8& lo, f16x8& hi, f32x4 c0, f32x4 c1, f32x4 s0,
+                                             f32x4 s1, float sgn) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     f16 a = lo[e], b = hi[e];
@@ -220,6 +218,14 @@ __device__ __forceinline__ void rope_rotate8(f16x8& lo, f16x8& hi, const float* 
     lo[e] = a;
     hi[e] = b;
   }
+}
+
+// The same with the 8 table entries c[e], s[e] read from memory (8
+// consecutive fp32 values each, 16-byte aligned).
+__device__ __forceinline__ void rope_rotate8(f16x8& lo, f16x8& hi, const float* c,
+                                             const float* s, float sgn) {
+  rope_rotate8(lo, hi, ((const f32x4*)c)[0], ((const f32x4*)c)[1], ((const f32x4*)s)[0],
+               ((const f32x4*)s)[1], sgn);
 }
 
 }  // namespace cgqa

@@ -196,3 +196,42 @@ def test_rope_workload_bitwise(gpu):
     torch.cuda.synchronize()
     assert _bits_equal(q, rope_fp16_ref(inp["q"].numpy(), pos, c, s))
     assert _bits_equal(k, rope_fp16_ref(inp["k"].numpy(), pos, c, s))
+
+
+def test_decode_step_with_rope(gpu):
+    """One rollout decode step with RoPE: attn_kv_append_rope stores the new
+    token's rotated key, attn_rope (ctx_lens) rotates its query, and
+    attn_decode_paged attends; the result must agree with the prefill that
+    rotates one-token chunks itself (two different kernels), and with the
+    oracle decode over the oracle-rotated tensors."""
+    from oracle import attn_decode_ref
+    prior = [0, 15, 16, 100, 1000, 2047]
+    inp = W.make_prefill_inputs(prior, [1] * len(prior), 16, 8, 128, seed=6400)
+    pos = chunk_positions(inp["cu_q"].numpy(), inp["ctx_lens"].numpy())
+    (c, s), tab = _tables(inp["max_ctx"], 128, gpu)
+    dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    kw = dict(max_ctx_len=inp["max_ctx"], max_q_len=1)
+    attn.kv_append(dd["k_new"], dd["v_new"], dd["cu_q"], dd["block_table"], dd["ctx_lens"],
+                   dd["k_pool"], dd["v_pool"], rope=tab, **kw)
+    op, _ = attn.prefill_paged(dd["q"], dd["k_pool"], dd["v_pool"], dd["block_table"],
+                               dd["ctx_lens"], dd["cu_q"], inp["scale"], rope=tab, **kw)
+    qd = dd["q"].clone()
+    attn.rope(qd, None, dd["cu_q"], tab, ctx_lens=dd["ctx_lens"], max_ctx_len=inp["max_ctx"],
+              max_seqlen=1)
+    od = attn.decode_paged(qd, dd["k_pool"], dd["v_pool"], dd["block_table"], dd["ctx_lens"],
+                           inp["scale"], max_ctx_len=inp["max_ctx"])
+    torch.cuda.synchronize()
+    qr = rope_fp16_ref(inp["q"].numpy(), pos, c, s)
+    assert _bits_equal(qd, qr)
+    kr = rope_fp16_ref(inp["k_new"].numpy(), pos, c, s)
+    kp, vp = kv_append_ref(inp["k_pool"].numpy(), inp["v_pool"].numpy(), kr,
+                           inp["v_new"].numpy(), inp["cu_q"].numpy(), inp["block_table"].numpy(),
+                           inp["ctx_lens"].numpy())
+    o_ref = attn_decode_ref(qr, kp, vp, inp["block_table"].numpy(), inp["ctx_lens"].numpy(),
+                            inp["scale"])
+    e_dec = max_abs(od.float().cpu().numpy(), o_ref)
+    e_pre = max_abs(op.float().cpu().numpy(), o_ref)
+    e_both = max_abs(od.float().cpu().numpy(), op.float().cpu().numpy())
+    print(f"decode with rope: decode {e_dec:.2e}, prefill {e_pre:.2e}, between {e_both:.2e}",
+          flush=True)
+    assert e_dec <= O_TOL and e_pre <= O_TOL and e_both <= 2 * O_TOL
