@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTE
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged",
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
             "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
-            "attn_sample", "attn_rope_tables_init", "attn_rope", "attn_kv_append_rope",
+            "attn_sample", "attn_rope_tables_init", "attn_rope", "attn_kv_append_rope", "attn_bwd_rope",
             "attn_prefill_paged_rope",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
@@ -122,6 +122,10 @@ def load_library():
     lib.attn_rope.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, ctypes.c_int32,
                               ctypes.POINTER(RopeTables), ctypes.c_int32, _vp]
     lib.attn_rope.restype = ctypes.c_int
+    lib.attn_bwd_rope.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.POINTER(RopeTables), _vp, _vp, _vp, ctypes.c_float, _vp,
+                                  ctypes.c_size_t, _vp]
+    lib.attn_bwd_rope.restype = ctypes.c_int
     lib.attn_kv_append_rope.argtypes = [ctypes.POINTER(PrefillDims), _vp, _vp, _vp, _vp, _vp,
                                         ctypes.POINTER(RopeTables), _vp, _vp, _vp]
     lib.attn_kv_append_rope.restype = ctypes.c_int
@@ -223,8 +227,10 @@ def bwd_workspace_bytes(dims):
 
 
 def bwd(q, k, v, o, lse, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None,
-        max_seqlen=None, workspace=None):
-    """attn_bwd: returns (dq, dk, dv) in fp16."""
+        max_seqlen=None, workspace=None, rope=None):
+    """attn_bwd: returns (dq, dk, dv) in fp16. rope=(cos, sin) calls
+    attn_bwd_rope: q and k are the rotated tensors and dq, dk come back
+    rotated to the unrotated ones (inverse RoPE fused into their stores)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.float16, 3)
@@ -253,6 +259,14 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens, scale=None, dq=None, dk=None, dv=None
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
+    if rope is not None:
+        tab = _rope_struct(rope, d=d, device=dev)
+        _check("attn_bwd_rope",
+               lib.attn_bwd_rope(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                 _ptr(lse), _ptr(dout), _ptr(cu_seqlens), ctypes.byref(tab),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), float(scale), _ptr(workspace),
+                                 workspace.numel(), _stream()))
+        return dq, dk, dv
     _check("attn_bwd", lib.attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                     _ptr(lse), _ptr(dout), _ptr(cu_seqlens), _ptr(dq),
                                     _ptr(dk), _ptr(dv), float(scale), _ptr(workspace),

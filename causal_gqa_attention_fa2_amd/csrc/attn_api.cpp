@@ -184,13 +184,15 @@ size_t attn_bwd_workspace_bytes(const attn_varlen_dims* dims) {
   return bwd_ws_bytes(dims);
 }
 
-attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k, const void* v,
-                     const void* o, const float* lse, const void* dO,
-                     const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float scale,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status bwd_impl(const attn_varlen_dims* dims, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* dO,
+                            const int32_t* cu_seqlens, const attn_rope_tables* rope, void* dq,
+                            void* dk, void* dv, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   bool empty = false;
   attn_status st = check_varlen(dims, &empty);
   if (st != ATTN_OK) return st;
+  if (rope && (st = check_rope(rope, dims->max_seqlen)) != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !cu_seqlens || !dq || !dk || !dv)
     return ATTN_ERR_INVALID_ARG;
@@ -223,7 +225,30 @@ attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.head_dim = dims->head_dim;
   a.scale = scale;
   a.num_cus = num_compute_units();
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.rope_max_pos = rope->max_pos;
+  }
   return cgqa::launch_bwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd(const attn_varlen_dims* dims, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dO,
+                     const int32_t* cu_seqlens, void* dq, void* dk, void* dv, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dims, q, k, v, o, lse, dO, cu_seqlens, nullptr, dq, dk, dv, scale, workspace,
+                  workspace_bytes, stream);
+}
+
+attn_status attn_bwd_rope(const attn_varlen_dims* dims, const void* q, const void* k,
+                          const void* v, const void* o, const float* lse, const void* dO,
+                          const int32_t* cu_seqlens, const attn_rope_tables* rope, void* dq,
+                          void* dk, void* dv, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!rope) return ATTN_ERR_INVALID_ARG;
+  return bwd_impl(dims, q, k, v, o, lse, dO, cu_seqlens, rope, dq, dk, dv, scale, workspace,
+                  workspace_bytes, stream);
 }
 
 size_t attn_decode_workspace_bytes(const attn_paged_dims* dims) {

@@ -74,11 +74,63 @@ struct BwdParams {
   f16* __restrict__ dv;
   f16* __restrict__ ds;      // workspace: fp16 dS blocks (32 x 32, lane-major)
   int nbmax;                 // 32-row blocks of the longest sequence
+  // RoPE tables [max_pos, D / 2] when dq and dk are rotated back at their
+  // stores (the ROPE kernels), else null.
+  const float* __restrict__ cos_t;
+  const float* __restrict__ sin_t;
+  int max_pos;
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles, n_ktiles;
   float scale, scale_log2;
 };
 
-template <int D>
+// Stores one lane's half of an fp32 accumulator row (element i of block db is
+// dimension 32 db + 8 (i / 4) + 4 hi + i % 4) as fp16, scaled by sc. ROPE:
+// the row is a gradient with respect to rotated q or k, and is carried back
+// to the unrotated tensor by the inverse rotation at position pos (dimension
+// j pairs with j + D/2, which is block db + D/64 of the same lane), with one
+// rounding to fp16 (rope_pair_f32).
+template <int D, bool ROPE>
+__device__ __forceinline__ void store_acc_row(f16* row, const f32x16* acc, float sc, int hi,
+                                              const BwdParams& p, int pos) {
+  constexpr int ND = D / 32;
+  if constexpr (ROPE) {
+    const int pp = min(pos, p.max_pos - 1);
+    const float* ct = p.cos_t + (size_t)pp * (D / 2) + 4 * hi;
+    const float* st = p.sin_t + (size_t)pp * (D / 2) + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < ND / 2; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 c = *(const f32x4*)(ct + 32 * db + 8 * r4);
+        const f32x4 s = *(const f32x4*)(st + 32 * db + 8 * r4);
+        f16x4 w1, w2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f16 a, b;
+          rope_pair_f32(acc[db][4 * r4 + e] * sc, acc[db + ND / 2][4 * r4 + e] * sc, c[e], -s[e],
+                        a, b);
+          w1[e] = a;
+          w2[e] = b;
+        }
+        *(f16x4*)(row + 32 * db + 8 * r4 + 4 * hi) = w1;
+        *(f16x4*)(row + 32 * (db + ND / 2) + 8 * r4 + 4 * hi) = w2;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (f16)(acc[db][4 * r4 + e] * sc);
+        *(f16x4*)(row + 32 * db + 8 * r4 + 4 * hi) = w;
+      }
+    }
+  }
+}
+
+template <int D, bool ROPE = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
@@ -317,16 +369,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
     // loads, so they drain first.
     if (rw.valid) {
       f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f16x4 wv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = (f16)(acc[db][4 * r4 + e] * p.scale);
-          *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = wv;
-        }
-      }
+      store_acc_row<D, ROPE>(dqrow, acc, p.scale, hi, p, rw.qpos);
       if (hi == 0) {
         p.drow[(size_t)rw.head * p.T + rw.qrow] = dsum;
         p.lse2[(size_t)rw.head * p.T + rw.qrow] = lse2;
@@ -346,7 +389,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   }
 }
 
-template <int D, bool STORE_DS>
+template <int D, bool STORE_DS, bool ROPE = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NT = D / 16;
   constexpr int ND = D / 32;
@@ -579,17 +622,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 
   if (key >= L) return;
   f16* dst = (team ? p.dk : p.dv) + ((size_t)(s0 + key) * p.h_kv + g) * D;
-  const float sc = team ? p.scale : 1.f;
-#pragma unroll
-  for (int db = 0; db < ND; ++db) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (f16)(acc[db][4 * r4 + e] * sc);
-      *(f16x4*)(dst + 32 * db + 8 * r4 + 4 * hi) = w;
-    }
-  }
+  if (ROPE && team)
+    store_acc_row<D, ROPE>(dst, acc, p.scale, hi, p, key);  // dK, rotated back
+  else
+    store_acc_row<D, false>(dst, acc, team ? p.scale : 1.f, hi, p, key);
 }
 
 
@@ -642,7 +678,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
 // natural key order: k-step u, half hi, slot s <-> key 16u + 8hi + s, both
 // for K^T (rows of the K tile) and for dS^T (the stored block's lanes
 // 32 hi' + key hold rows 8c + 4hi' + 0..3 in their 8-byte chunk c).
-template <int D>
+template <int D, bool ROPE = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
   constexpr int ND = D / 32;
   constexpr int CH = D / 8;
@@ -802,16 +838,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
     }
     if (rw.valid) {
       f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f16x4 wv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = (f16)(acc[db][4 * r4 + e] * p.scale);
-          *(f16x4*)(dqrow + 32 * db + 8 * r4 + 4 * hi) = wv;
-        }
-      }
+      store_acc_row<D, ROPE>(dqrow, acc, p.scale, hi, p, rw.qpos);
     }
     lds_barrier();
     ++round;
@@ -820,6 +847,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
     it = decode(nxt);
     rw = rows_of(it);
     issue_tile(it, rw, 0, 0);
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// Recompute path (ds = false): dq (which also forms the row terms) then
+// dK/dV. dS path: row terms, then dK/dV (which also stores dS), then dQ from
+// dS. ROPE: dq and dk are rotated back at their stores.
+template <int D, bool ROPE>
+void launch_bwd_kernels(const BwdParams& p, bool ds, dim3 gq, dim3 gk, dim3 gr,
+                        hipStream_t stream) {
+  if (!ds) {
+    hipLaunchKernelGGL((dq_kernel<D, ROPE>), gq, dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, false, ROPE>), gk, dim3(kBwdThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(bwd_rows_kernel<D>, gr, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, true, ROPE>), gk, dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((dq_ds_kernel<D, ROPE>), gq, dim3(kBwdThreads), 0, stream, p);
   }
 }
 
@@ -859,30 +906,26 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
   const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);  // persistent dq grids
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
-  if (a.ds == nullptr) {
-    // Recompute path: dq (which also forms the row terms) then dK/dV.
-    if (a.head_dim == 128) {
-      hipLaunchKernelGGL(dq_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<128, false>), gk, dim3(kBwdThreads), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL(dq_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<64, false>), gk, dim3(kBwdThreads), 0, stream, p);
-    }
+  const long long rows = (long long)a.total_tokens * a.h_q;
+  const int rpb = 256 / (a.head_dim / 8);
+  const long long wgs = (rows + rpb - 1) / rpb;
+  const dim3 gr((unsigned)(wgs < 4 * a.num_cus ? wgs : 4 * a.num_cus));
+  const bool ds = a.ds != nullptr;
+  if (a.rope_cos != nullptr) {
+    p.cos_t = a.rope_cos;
+    p.sin_t = a.rope_sin;
+    p.max_pos = a.rope_max_pos;
+    if (a.head_dim == 128)
+      launch_bwd_kernels<128, true>(p, ds, gq, gk, gr, stream);
+    else
+      launch_bwd_kernels<64, true>(p, ds, gq, gk, gr, stream);
   } else {
-    // dS path: row terms, then dK/dV (which also stores dS), then dQ from dS.
-    const long long rows = (long long)a.total_tokens * a.h_q;
-    const int rpb = 256 / (a.head_dim / 8);
-    const long long wgs = (rows + rpb - 1) / rpb;
-    const dim3 gr((unsigned)(wgs < 4 * a.num_cus ? wgs : 4 * a.num_cus));
-    if (a.head_dim == 128) {
-      hipLaunchKernelGGL(bwd_rows_kernel<128>, gr, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<128, true>), gk, dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL(dq_ds_kernel<128>, gq, dim3(kBwdThreads), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL(bwd_rows_kernel<64>, gr, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<64, true>), gk, dim3(kBwdThreads), 0, stream, p);
-      hipLaunchKernelGGL(dq_ds_kernel<64>, gq, dim3(kBwdThreads), 0, stream, p);
-    }
+    p.cos_t = p.sin_t = nullptr;
+    p.max_pos = 0;
+    if (a.head_dim == 128)
+      launch_bwd_kernels<128, false>(p, ds, gq, gk, gr, stream);
+    else
+      launch_bwd_kernels<64, false>(p, ds, gq, gk, gr, stream);
   }
   return hipGetLastError();
 }

@@ -206,6 +206,16 @@ __device__ __forceinline__ void rope_pair(f16& a, f16& b, float c, float s) {
   b = f64_to_f16_rn(y2);
 }
 
+// rope_pair for fp32 inputs (the backward's dq and dk accumulators): an
+// fp32 x fp32 product has 48 significant bits and is exact in fp64 too, so
+// the results are again the fp64 values of the formula rounded once to fp16.
+__device__ __forceinline__ void rope_pair_f32(float x1, float x2, float c, float s, f16& a,
+                                              f16& b) {
+  const double d1 = (double)x1, d2 = (double)x2, cd = (double)c, sd = (double)s;
+  a = f64_to_f16_rn(__builtin_fma(d1, cd, -(d2 * sd)));
+  b = f64_to_f16_rn(__builtin_fma(d2, cd, d1 * sd));
+}
+
 // rope_pair on the 8 pairs (lo[e], hi[e]), e = 0..7, with cosines c0, c1 and
 // sines s0, s1 (elements 0-3 and 4-7); sgn = -1 turns the other way (the
 // inverse rotation).

@@ -84,6 +84,11 @@ struct BwdArgs {
   float* drow;    // workspace: fp32 [h_q, T], rowsum(dO * O)
   float* lse2;    // workspace: fp32 [h_q, T], LSE * log2(e)
   void* ds = nullptr;  // workspace: fp16 dS blocks (the dS path), or null
+  // RoPE tables [rope_max_pos, head_dim / 2] to rotate dq and dk back with at
+  // their stores (q and k are the rotated tensors), or null.
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int rope_max_pos = 0;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   int num_cus;    // compute units of the device (persistent dq grid)
   float scale;

@@ -266,6 +266,22 @@ attn_status attn_rope(const attn_varlen_dims* dims, void* q, void* k, const int3
                       int32_t inverse, void* stream);
 
 /*
+ * attn_bwd_rope -- attn_bwd for attention whose q and k were rotated by
+ * attn_rope (ctx_lens = NULL): q and k here are the rotated tensors, and dq
+ * and dk are carried back to the unrotated ones by the inverse rotation at
+ * their stores (token i of a sequence at position i), each value rounded
+ * once to fp16 from the fp32 gradient; dv is as attn_bwd's. It replaces
+ * attn_bwd followed by attn_rope(..., inverse = 1) on dq and dk, which rounds
+ * twice (results agree to about one fp16 unit). Same workspace as attn_bwd;
+ * rope->max_pos >= max_seqlen.
+ */
+attn_status attn_bwd_rope(const attn_varlen_dims* dims, const void* q, const void* k,
+                          const void* v, const void* o, const float* lse, const void* dO,
+                          const int32_t* cu_seqlens, const attn_rope_tables* rope, void* dq,
+                          void* dk, void* dv, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * attn_kv_append_rope -- attn_kv_append that rotates each new key by its
  * context position on its way into the pool (values are copied as they
  * are). The pool then holds the same bits as attn_rope on k_new (with

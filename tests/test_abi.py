@@ -345,3 +345,21 @@ def test_rope_argument_checks(lib):
         assert fn(dims(), tab(mp=1000)) == INVALID  # tables shorter than max_ctx_len
         assert fn(dims(), tab(c=FAKE + 4)) == INVALID
         assert fn(dims(n=0, tq=0, mq=0), tab()) == OK
+
+
+def test_bwd_rope_argument_checks(lib):
+    """attn_bwd_rope: tables required and long enough; otherwise attn_bwd's
+    checks (empty batch is a no-op)."""
+    from causal_gqa_attention_fa2_amd.attn import RopeTables
+    p = ctypes.c_void_p
+    dims = VarlenDims(2, 100, 60, 16, 8, 128)
+
+    def call(dm, t, ws_bytes=1 << 30):
+        return lib.attn_bwd_rope(ctypes.byref(dm), *([p(FAKE)] * 7), t, p(FAKE), p(FAKE),
+                                 p(FAKE), 0.1, p(FAKE), ws_bytes, None)
+
+    assert call(dims, None) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE, 59))) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE + 4, 100))) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE, 100)), ws_bytes=0) == WORKSPACE
+    assert call(VarlenDims(0, 0, 0, 16, 8, 128), ctypes.byref(RopeTables(FAKE, FAKE, 100))) == OK

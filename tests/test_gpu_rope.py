@@ -235,3 +235,45 @@ def test_decode_step_with_rope(gpu):
     print(f"decode with rope: decode {e_dec:.2e}, prefill {e_pre:.2e}, between {e_both:.2e}",
           flush=True)
     assert e_dec <= O_TOL and e_pre <= O_TOL and e_both <= 2 * O_TOL
+
+
+@pytest.mark.parametrize("seqs,h_q,h_kv,d", [
+    ([1, 17, 64, 65, 130, 0, 33], 16, 8, 128),  # ragged: the dS path
+    ([128, 128], 16, 8, 128),                   # equal lengths: the recompute path
+    ([300, 64, 1], 8, 2, 64),
+    ([256, 256], 8, 2, 64),
+], ids=lambda x: str(x))
+def test_bwd_with_fused_inverse_rope(gpu, seqs, h_q, h_kv, d):
+    """attn_bwd_rope (inverse rotation of dq, dk at their stores, one fp16
+    rounding) against the oracle chain within the gradient bar, no less
+    accurate than attn_bwd + inverse attn_rope (two roundings) and within
+    about one fp16 unit of it; dv is attn_bwd's bit for bit."""
+    inp = W.make_train_inputs(seqs, h_q, h_kv, d, seed=6500 + sum(seqs) + d)
+    ms = max(seqs)
+    pos = varlen_positions(inp["cu_seqlens"].numpy())
+    (c, s), tab = _tables(ms, d, gpu)
+    dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q, k = dd["q"].clone(), dd["k"].clone()
+    attn.rope(q, k, dd["cu_seqlens"], tab, max_seqlen=ms)
+    o, lse = attn.fwd(q, k, dd["v"], dd["cu_seqlens"], inp["scale"], max_seqlen=ms)
+    args = (q, k, dd["v"], o, lse, dd["dout"], dd["cu_seqlens"], inp["scale"])
+    dq1, dk1, dv1 = attn.bwd(*args, max_seqlen=ms, rope=tab)
+    dq2, dk2, dv2 = attn.bwd(*args, max_seqlen=ms)
+    attn.rope(dq2, dk2, dd["cu_seqlens"], tab, max_seqlen=ms, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dv1, dv2)
+
+    qr = rope_fp16_ref(inp["q"].numpy(), pos, c, s)
+    kr = rope_fp16_ref(inp["k"].numpy(), pos, c, s)
+    cu = inp["cu_seqlens"].numpy()
+    dq_r, dk_r, _ = attn_bwd_ref(qr, kr, inp["v"].numpy(), inp["dout"].numpy(), cu,
+                                 inp["scale"])
+    dq_ref = rope_ref(dq_r, pos, c, s, inverse=True)
+    dk_ref = rope_ref(dk_r, pos, c, s, inverse=True)
+    res = []
+    for name, fused, unfused, ref in (("dq", dq1, dq2, dq_ref), ("dk", dk1, dk2, dk_ref)):
+        f, u = fused.float().cpu().numpy(), unfused.float().cpu().numpy()
+        e_f, e_u, between = rel_l2(f, ref), rel_l2(u, ref), rel_l2(f, u)
+        res.append(f"{name} fused {e_f:.2e} unfused {e_u:.2e} between {between:.2e}")
+        assert e_f <= GRAD_TOL and e_f <= e_u * 1.02 + 1e-6 and between <= 1e-3, res[-1]
+    print(f"bwd rope {seqs} d{d}: " + "; ".join(res), flush=True)
