@@ -196,9 +196,10 @@ def bench_prefill(attn, W, dev, iters):
 def bench_rope(attn, W, dev, iters):
     """RoPE, timed on its own (not part of `value`): the standalone pass over
     the training batch's q and k (qwen3_train: 8 x 1024 tokens, 16 + 8 heads,
-    d = 128), forward and inverse, HBM-bound against 8 TB/s; and on the
-    paged_prefill workload the append and the prefill with the rotation
-    fused in, beside the same calls without it."""
+    d = 128), forward and inverse, HBM-bound against 8 TB/s; the training
+    backward with the inverse rotation fused into its dq / dk stores, beside
+    attn_bwd alone; and on the paged_prefill workload the append and the
+    prefill with the rotation fused in, beside the same calls without it."""
     import torch
     inp = W.workload_inputs(TRAIN_WORKLOAD, with_dout=False)
     q, k, cu = inp["q"].to(dev), inp["k"].to(dev), inp["cu_seqlens"].to(dev)
@@ -228,6 +229,20 @@ def bench_rope(attn, W, dev, iters):
            "fwd_us": round(t_f * 1e6, 2), "fwd_GB/s": round(nbytes / t_f / 1e9, 1),
            "inv_us": round(t_i * 1e6, 2), "inv_GB/s": round(nbytes / t_i / 1e9, 1),
            "fwd_hbm_peak_frac": round(nbytes / t_f / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # Training backward on the rotated q and k: attn_bwd_rope (inverse rotation
+    # of dq, dk fused into the stores) against attn_bwd alone.
+    tr_v = W.workload_inputs(TRAIN_WORKLOAD)
+    v, dout = tr_v["v"].to(dev), tr_v["dout"].to(dev)
+    o, lse = attn.fwd(q, k, v, cu, inp["scale"], max_seqlen=ms)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(max(1, attn.bwd_workspace_bytes(attn.varlen_dims(q, k, cu, ms))),
+                     dtype=torch.uint8, device=dev)
+    bargs = (q, k, v, o, lse, dout, cu, inp["scale"])
+    t_b = timed(lambda: attn.bwd(*bargs, dq=dq, dk=dk, dv=dv, max_seqlen=ms, workspace=ws))
+    t_br = timed(lambda: attn.bwd(*bargs, dq=dq, dk=dk, dv=dv, max_seqlen=ms, workspace=ws,
+                                  rope=tab))
+    out.update({"bwd_us": round(t_b * 1e6, 2), "bwd_rope_us": round(t_br * 1e6, 2)})
 
     qp, kn, vn, cq, kp, vp, bt, ctx = (pre[n].to(dev) for n in (
         "q", "k_new", "v_new", "cu_q", "k_pool", "v_pool", "block_table", "ctx_lens"))

@@ -87,8 +87,8 @@ struct BwdParams {
 // dimension 32 db + 8 (i / 4) + 4 hi + i % 4) as fp16, scaled by sc. ROPE:
 // the row is a gradient with respect to rotated q or k, and is carried back
 // to the unrotated tensor by the inverse rotation at position pos (dimension
-// j pairs with j + D/2, which is block db + D/64 of the same lane), with one
-// rounding to fp16 (rope_pair_f32).
+// j pairs with j + D/2, which is block db + D/64 of the same lane), in fp32
+// and rounded to fp16 once (rope_pair_f32).
 template <int D, bool ROPE>
 __device__ __forceinline__ void store_acc_row(f16* row, const f32x16* acc, float sc, int hi,
                                               const BwdParams& p, int pos) {
@@ -97,24 +97,31 @@ __device__ __forceinline__ void store_acc_row(f16* row, const f32x16* acc, float
     const int pp = min(pos, p.max_pos - 1);
     const float* ct = p.cos_t + (size_t)pp * (D / 2) + 4 * hi;
     const float* st = p.sin_t + (size_t)pp * (D / 2) + 4 * hi;
+    // All values first, then the stores back to back in address order (as
+    // the plain path issues them), so that each row's lines are completed
+    // while they are still in L2.
+    f16x4 w[ND][4];
 #pragma unroll
     for (int db = 0; db < ND / 2; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 c = *(const f32x4*)(ct + 32 * db + 8 * r4);
         const f32x4 s = *(const f32x4*)(st + 32 * db + 8 * r4);
-        f16x4 w1, w2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           f16 a, b;
           rope_pair_f32(acc[db][4 * r4 + e] * sc, acc[db + ND / 2][4 * r4 + e] * sc, c[e], -s[e],
                         a, b);
-          w1[e] = a;
-          w2[e] = b;
+          w[db][r4][e] = a;
+          w[db + ND / 2][r4][e] = b;
         }
-        *(f16x4*)(row + 32 * db + 8 * r4 + 4 * hi) = w1;
-        *(f16x4*)(row + 32 * (db + ND / 2) + 8 * r4 + 4 * hi) = w2;
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *(f16x4*)(row + 32 * db + 8 * r4 + 4 * hi) = w[db][r4];
     }
   } else {
 #pragma unroll

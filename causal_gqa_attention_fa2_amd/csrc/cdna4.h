@@ -206,14 +206,16 @@ __device__ __forceinline__ void rope_pair(f16& a, f16& b, float c, float s) {
   b = f64_to_f16_rn(y2);
 }
 
-// rope_pair for fp32 inputs (the backward's dq and dk accumulators): an
-// fp32 x fp32 product has 48 significant bits and is exact in fp64 too, so
-// the results are again the fp64 values of the formula rounded once to fp16.
+// The rotation of rope_pair for fp32 inputs (the backward's dq and dk
+// accumulators, rotated back with -s), in fp32: each output is one fma over
+// one rounded product, then rounded to fp16, so it is within one fp16 unit
+// of the correctly rounded value and almost always equal to it. Gradients
+// need no bit-exact rotation, and the fp64 form of rope_pair cost the
+// backward's epilogues as much as a separate inverse pass.
 __device__ __forceinline__ void rope_pair_f32(float x1, float x2, float c, float s, f16& a,
                                               f16& b) {
-  const double d1 = (double)x1, d2 = (double)x2, cd = (double)c, sd = (double)s;
-  a = f64_to_f16_rn(__builtin_fma(d1, cd, -(d2 * sd)));
-  b = f64_to_f16_rn(__builtin_fma(d2, cd, d1 * sd));
+  a = (f16)__builtin_fmaf(x1, c, -(x2 * s));
+  b = (f16)__builtin_fmaf(x2, c, x1 * s);
 }
 
 // rope_pair on the 8 pairs (lo[e], hi[e]), e = 0..7, with cosines c0, c1 and

@@ -269,11 +269,13 @@ attn_status attn_rope(const attn_varlen_dims* dims, void* q, void* k, const int3
  * attn_bwd_rope -- attn_bwd for attention whose q and k were rotated by
  * attn_rope (ctx_lens = NULL): q and k here are the rotated tensors, and dq
  * and dk are carried back to the unrotated ones by the inverse rotation at
- * their stores (token i of a sequence at position i), each value rounded
- * once to fp16 from the fp32 gradient; dv is as attn_bwd's. It replaces
- * attn_bwd followed by attn_rope(..., inverse = 1) on dq and dk, which rounds
- * twice (results agree to about one fp16 unit). Same workspace as attn_bwd;
- * rope->max_pos >= max_seqlen.
+ * their stores (token i of a sequence at position i), computed in fp32 from
+ * the fp32 gradient and rounded once to fp16; dv is as attn_bwd's. It
+ * replaces attn_bwd followed by attn_rope(..., inverse = 1) on dq and dk,
+ * which rounds to fp16 twice (results agree to about one fp16 unit; unlike
+ * the forward rotations this one is not bit-exact against a correctly
+ * rounded reference). Same workspace as attn_bwd; rope->max_pos >=
+ * max_seqlen.
  */
 attn_status attn_bwd_rope(const attn_varlen_dims* dims, const void* q, const void* k,
                           const void* v, const void* o, const float* lse, const void* dO,

@@ -244,9 +244,9 @@ def test_decode_step_with_rope(gpu):
     ([256, 256], 8, 2, 64),
 ], ids=lambda x: str(x))
 def test_bwd_with_fused_inverse_rope(gpu, seqs, h_q, h_kv, d):
-    """attn_bwd_rope (inverse rotation of dq, dk at their stores, one fp16
-    rounding) against the oracle chain within the gradient bar, no less
-    accurate than attn_bwd + inverse attn_rope (two roundings) and within
+    """attn_bwd_rope (inverse rotation of dq, dk in fp32 at their stores, one
+    fp16 rounding) against the oracle chain within the gradient bar, no less
+    accurate than attn_bwd + inverse attn_rope (two fp16 roundings) and within
     about one fp16 unit of it; dv is attn_bwd's bit for bit."""
     inp = W.make_train_inputs(seqs, h_q, h_kv, d, seed=6500 + sum(seqs) + d)
     ms = max(seqs)
