@@ -277,3 +277,82 @@ def test_bwd_with_fused_inverse_rope(gpu, seqs, h_q, h_kv, d):
         res.append(f"{name} fused {e_f:.2e} unfused {e_u:.2e} between {between:.2e}")
         assert e_f <= GRAD_TOL and e_f <= e_u * 1.02 + 1e-6 and between <= 1e-3, res[-1]
     print(f"bwd rope {seqs} d{d}: " + "; ".join(res), flush=True)
+
+
+def test_rope_prefill_workload(gpu):
+    """The paged_prefill workload (32 sequences, cached 0-1536, new 128-512
+    tokens) with RoPE, launched as the benchmark launches it: the pools
+    against the oracle's append of the oracle-rotated keys (every element),
+    the fused prefill against attn_rope + attn_prefill_paged (bit for bit) and
+    against the oracle on sampled sequences."""
+    inp = W.prefill_workload_inputs("paged_prefill")
+    pos = chunk_positions(inp["cu_q"].numpy(), inp["ctx_lens"].numpy())
+    (c, s), tab = _tables(inp["max_ctx"], inp["d"], gpu)
+    dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    kw = dict(max_ctx_len=inp["max_ctx"], max_q_len=inp["max_q_len"])
+    attn.kv_append(dd["k_new"], dd["v_new"], dd["cu_q"], dd["block_table"], dd["ctx_lens"],
+                   dd["k_pool"], dd["v_pool"], rope=tab, **kw)
+    o, lse = attn.prefill_paged(dd["q"], dd["k_pool"], dd["v_pool"], dd["block_table"],
+                                dd["ctx_lens"], dd["cu_q"], inp["scale"], rope=tab, **kw)
+    q2 = dd["q"].clone()
+    attn.rope(q2, None, dd["cu_q"], tab, ctx_lens=dd["ctx_lens"], max_ctx_len=inp["max_ctx"],
+              max_seqlen=inp["max_q_len"])
+    o2, lse2 = attn.prefill_paged(q2, dd["k_pool"], dd["v_pool"], dd["block_table"],
+                                  dd["ctx_lens"], dd["cu_q"], inp["scale"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    qr = rope_fp16_ref(inp["q"].numpy(), pos, c, s)
+    assert _bits_equal(q2, qr)
+    kr = rope_fp16_ref(inp["k_new"].numpy(), pos, c, s)
+    kp, vp = kv_append_ref(inp["k_pool"].numpy(), inp["v_pool"].numpy(), kr,
+                           inp["v_new"].numpy(), inp["cu_q"].numpy(), inp["block_table"].numpy(),
+                           inp["ctx_lens"].numpy())
+    assert _bits_equal(dd["k_pool"], kp) and _bits_equal(dd["v_pool"], vp)
+    cu = inp["cu_q"].tolist()
+    o_np, lse_np = o.float().cpu().numpy(), lse.cpu().numpy()
+    worst_o = worst_l = 0.0
+    for b in (0, 9, 20, 31):
+        st, en = cu[b], cu[b + 1]
+        o_ref, lse_ref = attn_prefill_ref(qr[st:en], kp, vp, inp["block_table"].numpy()[b:b + 1],
+                                          [int(inp["ctx_lens"][b])], [0, en - st], inp["scale"])
+        worst_o = max(worst_o, max_abs(o_np[st:en], o_ref))
+        worst_l = max(worst_l, max_abs(lse_np[:, st:en], lse_ref))
+    print(f"paged_prefill with rope: O {worst_o:.2e}, LSE {worst_l:.2e}", flush=True)
+    assert worst_o <= O_TOL and worst_l <= LSE_TOL
+
+
+def test_bwd_rope_workload(gpu):
+    """qwen3_train (8 x 1024, H_q 16, H_kv 8, d 128) through attn_bwd_rope as
+    the benchmark launches it, against attn_bwd + inverse attn_rope (about one
+    fp16 unit apart) and dv bit for bit; the oracle on one sampled sequence
+    and KV group."""
+    inp = W.workload_inputs("qwen3_train")
+    ms = inp["max_seqlen"]
+    (c, s), tab = _tables(ms, inp["d"], gpu)
+    dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    q, k = dd["q"].clone(), dd["k"].clone()
+    attn.rope(q, k, dd["cu_seqlens"], tab, max_seqlen=ms)
+    o, lse = attn.fwd(q, k, dd["v"], dd["cu_seqlens"], inp["scale"], max_seqlen=ms)
+    args = (q, k, dd["v"], o, lse, dd["dout"], dd["cu_seqlens"], inp["scale"])
+    dq1, dk1, dv1 = attn.bwd(*args, max_seqlen=ms, rope=tab)
+    dq2, dk2, dv2 = attn.bwd(*args, max_seqlen=ms)
+    attn.rope(dq2, dk2, dd["cu_seqlens"], tab, max_seqlen=ms, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dv1, dv2)
+    for a, b in ((dq1, dq2), (dk1, dk2)):
+        assert rel_l2(a.float().cpu().numpy(), b.float().cpu().numpy()) <= 1e-3
+    # Oracle: sequence 5, KV head 3 and its two query heads.
+    seq, g = 5, 3
+    rows = slice(seq * 1024, (seq + 1) * 1024)
+    heads = slice(2 * g, 2 * g + 2)
+    pos = np.arange(1024)
+    qr = q[rows, heads].cpu().numpy()
+    kr = k[rows, g:g + 1].cpu().numpy()
+    cu1 = np.array([0, 1024])
+    dq_r, dk_r, _ = attn_bwd_ref(qr, kr, inp["v"].numpy()[rows, g:g + 1],
+                                 inp["dout"].numpy()[rows, heads], cu1, inp["scale"])
+    e_q = rel_l2(dq1[rows, heads].float().cpu().numpy(), rope_ref(dq_r, pos, c, s, inverse=True))
+    # dK sums over the group's query heads; with G = 2 both are in the sample.
+    e_k = rel_l2(dk1[rows, g:g + 1].float().cpu().numpy(), rope_ref(dk_r, pos, c, s, inverse=True))
+    print(f"qwen3_train bwd rope: dq {e_q:.2e}, dk {e_k:.2e}", flush=True)
+    assert e_q <= GRAD_TOL and e_k <= GRAD_TOL
