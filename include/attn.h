@@ -230,9 +230,15 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
  * j + d/2 by the angle pos * theta_j,
  *   x'_j = x_j cos - x_{j+d/2} sin,   x'_{j+d/2} = x_{j+d/2} cos + x_j sin,
  * with cos / sin read from caller-owned fp32 tables [max_pos, d/2] (device
- * pointers, 16-byte aligned; row p holds position p). Every kernel rotates
- * in fp64 and rounds once to fp16, so the rotated values are the same bits
- * whichever entry point rotates them.
+ * pointers, 16-byte aligned; row p holds position p; the library only reads
+ * them). The rotations of q and k (attn_rope, attn_kv_append_rope,
+ * attn_prefill_paged_rope) are computed in fp64 and rounded once to fp16, so
+ * their results are the same bits whichever entry point rotates; the inverse
+ * rotation inside attn_bwd_rope works in fp32 (see there).
+ * Errors of every RoPE entry point: ATTN_ERR_INVALID_ARG when rope is NULL,
+ * a table pointer is NULL or not 16-byte aligned, max_pos < 1, or max_pos
+ * does not cover the positions the call can form; all other checks are
+ * those of the entry point without RoPE, made before any HIP call.
  */
 typedef struct attn_rope_tables {
     const float* cos;
