@@ -24,6 +24,7 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_pag
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
             "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
             "attn_sample", "attn_rope_tables_init", "attn_rope", "attn_kv_append_rope", "attn_bwd_rope",
+            "attn_decode_paged_rope",
             "attn_prefill_paged_rope",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
@@ -122,6 +123,10 @@ def load_library():
     lib.attn_rope.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, ctypes.c_int32,
                               ctypes.POINTER(RopeTables), ctypes.c_int32, _vp]
     lib.attn_rope.restype = ctypes.c_int
+    lib.attn_decode_paged_rope.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp, _vp, _vp, _vp,
+                                           ctypes.POINTER(RopeTables), _vp, ctypes.c_float, _vp,
+                                           ctypes.c_size_t, _vp]
+    lib.attn_decode_paged_rope.restype = ctypes.c_int
     lib.attn_bwd_rope.argtypes = [ctypes.POINTER(VarlenDims), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   ctypes.POINTER(RopeTables), _vp, _vp, _vp, ctypes.c_float, _vp,
                                   ctypes.c_size_t, _vp]
@@ -285,8 +290,10 @@ def decode_workspace_bytes(dims):
 
 
 def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, scale=None, o=None,
-                 max_ctx_len=None, workspace=None):
-    """attn_decode_paged: returns o fp16 [n, h_q, d]."""
+                 max_ctx_len=None, workspace=None, rope=None):
+    """attn_decode_paged: returns o fp16 [n, h_q, d]. rope=(cos, sin) calls
+    attn_decode_paged_rope, which rotates each query by its position
+    ctx_lens[b] - 1 as it loads it (q is not modified)."""
     lib = load_library()
     dev = q.device
     _need(q, "q", torch.float16, 3)
@@ -313,6 +320,14 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, scale=None, o=None,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
+    if rope is not None:
+        tab = _rope_struct(rope, d=d, device=dev)
+        _check("attn_decode_paged_rope",
+               lib.attn_decode_paged_rope(ctypes.byref(dims), _ptr(q), _ptr(k_pool),
+                                          _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens),
+                                          ctypes.byref(tab), _ptr(o), float(scale),
+                                          _ptr(workspace), workspace.numel(), _stream()))
+        return o
     _check("attn_decode_paged",
            lib.attn_decode_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                  _ptr(block_table), _ptr(ctx_lens), _ptr(o), float(scale),

@@ -258,13 +258,15 @@ size_t attn_decode_workspace_bytes(const attn_paged_dims* dims) {
   return decode_ws_parts(dims, &ob, &mb);
 }
 
-attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
-                              const void* v_pool, const int32_t* block_table,
-                              const int32_t* ctx_lens, void* o, float scale, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+static attn_status decode_impl(const attn_paged_dims* dims, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* ctx_lens, const attn_rope_tables* rope, void* o,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   bool empty = false;
   attn_status st = check_paged(dims, &empty);
   if (st != ATTN_OK) return st;
+  if (rope && (st = check_rope(rope, dims->max_ctx_len)) != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   if (!q || !ctx_lens || !o) return ATTN_ERR_INVALID_ARG;
   if (dims->max_ctx_len > 0 && (!k_pool || !v_pool || !block_table)) return ATTN_ERR_INVALID_ARG;
@@ -292,7 +294,30 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
   a.max_blocks_per_seq = dims->max_blocks_per_seq;
   a.n_wgs = cgqa::decode_num_wgs(dims->n_seqs, dims->max_ctx_len);
   a.scale = scale;
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.rope_max_pos = rope->max_pos;
+  }
   return cgqa::launch_decode(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* ctx_lens, void* o, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, nullptr, o, scale, workspace,
+                     workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_rope(const attn_paged_dims* dims, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* ctx_lens,
+                                   const attn_rope_tables* rope, void* o, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!rope) return ATTN_ERR_INVALID_ARG;
+  return decode_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, rope, o, scale, workspace,
+                     workspace_bytes, stream);
 }
 
 static attn_status kv_append_impl(const attn_prefill_dims* dims, const void* k_new,

@@ -52,6 +52,11 @@ struct DecParams {
   int32_t* __restrict__ wg_first;   // [n_wgs]
   int n, h_q, h_kv, G, max_blocks, n_wgs;
   float scale_log2;
+  // RoPE tables [max_pos, D / 2] to rotate each query by its position
+  // ctx - 1 as it is loaded, or null.
+  const float* __restrict__ cos_t;
+  const float* __restrict__ sin_t;
+  int max_pos;
 };
 
 struct SoftState {
@@ -166,6 +171,27 @@ __device__ __forceinline__ void gather_segment(const DecParams& p, int b, int g,
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qh[h] = *(const u32x4*)(p.q + ((size_t)b * p.h_q + g * G + h) * D + dc * 8);
+  if (p.cos_t != nullptr) {
+    // RoPE of the query at position ctx - 1: chunk dc pairs with chunk
+    // dc ^ (LPR / 2) (dimensions D/2 apart), which lane ^ (LPR / 2) holds.
+    // Both lanes rotate the pair (rope_pair, exact) and keep their half.
+    const int pos = min(max(t_end - 1, 0), p.max_pos - 1);
+    const bool low = dc < LPR / 2;
+    const int j0c = 8 * (dc % (LPR / 2));
+    const float* ct = p.cos_t + (size_t)pos * (D / 2) + j0c;
+    const float* st = p.sin_t + (size_t)pos * (D / 2) + j0c;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      u32x4 other;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) other[e] = (uint32_t)__shfl_xor((int)qh[h][e], LPR / 2, 64);
+      const f16x8 mine = __builtin_bit_cast(f16x8, qh[h]);
+      const f16x8 part = __builtin_bit_cast(f16x8, other);
+      f16x8 lo = low ? mine : part, hi = low ? part : mine;
+      rope_rotate8(lo, hi, ct, st, 1.f);
+      qh[h] = __builtin_bit_cast(u32x4, low ? lo : hi);
+    }
+  }
   SoftState st[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -416,6 +442,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.max_blocks = a.max_blocks_per_seq;
   p.n_wgs = a.n_wgs;
   p.scale_log2 = a.scale * kLog2e;
+  p.cos_t = a.rope_cos;
+  p.sin_t = a.rope_sin;
+  p.max_pos = a.rope_max_pos;
   if (p.G > kMaxG) return hipErrorInvalidValue;
   return a.head_dim == 128 ? launch_d<128>(p, p.G, stream) : launch_d<64>(p, p.G, stream);
 }

@@ -106,6 +106,11 @@ struct DecodeArgs {
   int32_t* plan;   // workspace: int32 [n + 1] block prefix sums, [n_wgs] first sequences
   int n_seqs, h_q, h_kv, head_dim, max_blocks_per_seq, n_wgs;
   float scale;
+  // RoPE tables [rope_max_pos, head_dim / 2] to rotate each query by its
+  // position ctx - 1 as it is loaded, or null.
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  int rope_max_pos = 0;
 };
 
 // Work-groups of the paged-decode gather: the flattened (sequence, block)

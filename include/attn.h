@@ -232,7 +232,8 @@ attn_status attn_prefill_paged(const attn_prefill_dims* dims, const void* q, con
  * with cos / sin read from caller-owned fp32 tables [max_pos, d/2] (device
  * pointers, 16-byte aligned; row p holds position p; the library only reads
  * them). The rotations of q and k (attn_rope, attn_kv_append_rope,
- * attn_prefill_paged_rope) are computed in fp64 and rounded once to fp16, so
+ * attn_prefill_paged_rope, attn_decode_paged_rope) are computed in fp64 and
+ * rounded once to fp16, so
  * their results are the same bits whichever entry point rotates; the inverse
  * rotation inside attn_bwd_rope works in fp32 (see there).
  * Errors of every RoPE entry point: ATTN_ERR_INVALID_ARG when rope is NULL,
@@ -288,6 +289,20 @@ attn_status attn_bwd_rope(const attn_varlen_dims* dims, const void* q, const voi
                           const int32_t* cu_seqlens, const attn_rope_tables* rope, void* dq,
                           void* dk, void* dv, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_rope -- attn_decode_paged whose queries are rotated by
+ * their positions ctx_lens[b] - 1 (the token being decoded is the last of
+ * its context) as they are loaded; q itself is not modified, and the keys
+ * in the pool are taken as already rotated (attn_kv_append_rope). O is
+ * bitwise that of attn_rope on q (ctx_lens, one token per sequence)
+ * followed by attn_decode_paged. rope->max_pos >= max_ctx_len.
+ */
+attn_status attn_decode_paged_rope(const attn_paged_dims* dims, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* ctx_lens,
+                                   const attn_rope_tables* rope, void* o, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_kv_append_rope -- attn_kv_append that rotates each new key by its

@@ -363,3 +363,21 @@ def test_bwd_rope_argument_checks(lib):
     assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE + 4, 100))) == INVALID
     assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE, 100)), ws_bytes=0) == WORKSPACE
     assert call(VarlenDims(0, 0, 0, 16, 8, 128), ctypes.byref(RopeTables(FAKE, FAKE, 100))) == OK
+
+
+def test_decode_rope_argument_checks(lib):
+    """attn_decode_paged_rope: tables required and covering max_ctx_len."""
+    from causal_gqa_attention_fa2_amd.attn import RopeTables
+    p = ctypes.c_void_p
+    dims = PagedDims(4, 16, 8, 128, 16, 64, 1000, 1024)
+
+    def call(dm, t, ws_bytes=1 << 30):
+        return lib.attn_decode_paged_rope(ctypes.byref(dm), *([p(FAKE)] * 5), t, p(FAKE), 0.1,
+                                          p(FAKE), ws_bytes, None)
+
+    assert call(dims, None) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE, 1000))) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE + 8, FAKE, 2048))) == INVALID
+    assert call(dims, ctypes.byref(RopeTables(FAKE, FAKE, 2048)), ws_bytes=0) == WORKSPACE
+    assert call(PagedDims(0, 16, 8, 128, 16, 64, 1000, 1024),
+                ctypes.byref(RopeTables(FAKE, FAKE, 2048))) == OK

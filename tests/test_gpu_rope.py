@@ -201,9 +201,10 @@ def test_rope_workload_bitwise(gpu):
 def test_decode_step_with_rope(gpu):
     """One rollout decode step with RoPE: attn_kv_append_rope stores the new
     token's rotated key, attn_rope (ctx_lens) rotates its query, and
-    attn_decode_paged attends; the result must agree with the prefill that
-    rotates one-token chunks itself (two different kernels), and with the
-    oracle decode over the oracle-rotated tensors."""
+    attn_decode_paged attends; attn_decode_paged_rope (rotating the query at
+    load) must give the same bits. The result must agree with the prefill
+    that rotates one-token chunks itself (two different kernels), and with
+    the oracle decode over the oracle-rotated tensors."""
     from oracle import attn_decode_ref
     prior = [0, 15, 16, 100, 1000, 2047]
     inp = W.make_prefill_inputs(prior, [1] * len(prior), 16, 8, 128, seed=6400)
@@ -220,7 +221,12 @@ def test_decode_step_with_rope(gpu):
               max_seqlen=1)
     od = attn.decode_paged(qd, dd["k_pool"], dd["v_pool"], dd["block_table"], dd["ctx_lens"],
                            inp["scale"], max_ctx_len=inp["max_ctx"])
+    # The decode that rotates its queries itself: the same bits.
+    of = attn.decode_paged(dd["q"], dd["k_pool"], dd["v_pool"], dd["block_table"],
+                           dd["ctx_lens"], inp["scale"], max_ctx_len=inp["max_ctx"], rope=tab)
     torch.cuda.synchronize()
+    assert torch.equal(of, od)
+    assert torch.equal(dd["q"].cpu(), inp["q"])
     qr = rope_fp16_ref(inp["q"].numpy(), pos, c, s)
     assert _bits_equal(qd, qr)
     kr = rope_fp16_ref(inp["k_new"].numpy(), pos, c, s)
@@ -356,3 +362,34 @@ def test_bwd_rope_workload(gpu):
     e_k = rel_l2(dk1[rows, g:g + 1].float().cpu().numpy(), rope_ref(dk_r, pos, c, s, inverse=True))
     print(f"qwen3_train bwd rope: dq {e_q:.2e}, dk {e_k:.2e}", flush=True)
     assert e_q <= GRAD_TOL and e_k <= GRAD_TOL
+
+
+def test_decode_rope_workload(gpu):
+    """The paged_decode workload (256 sequences, context 128-4096) with RoPE,
+    launched as the benchmark launches it: attn_decode_paged_rope equals
+    attn_rope on q followed by attn_decode_paged bit for bit, and matches the
+    oracle decode on sampled sequences."""
+    from oracle import attn_decode_ref
+    inp = W.decode_workload_inputs("paged_decode")
+    n = inp["q"].shape[0]
+    ctx = inp["ctx_lens"].numpy()
+    (c, s), tab = _tables(int(ctx.max()), inp["q"].shape[2], gpu)
+    dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    of = attn.decode_paged(dd["q"], dd["k_pool"], dd["v_pool"], dd["block_table"],
+                           dd["ctx_lens"], inp["scale"], max_ctx_len=int(ctx.max()), rope=tab)
+    cu1 = torch.arange(n + 1, dtype=torch.int32, device=gpu)
+    qd = dd["q"].clone()
+    attn.rope(qd, None, cu1, tab, ctx_lens=dd["ctx_lens"], max_ctx_len=int(ctx.max()),
+              max_seqlen=1)
+    od = attn.decode_paged(qd, dd["k_pool"], dd["v_pool"], dd["block_table"], dd["ctx_lens"],
+                           inp["scale"], max_ctx_len=int(ctx.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(of, od)
+    qr = rope_fp16_ref(inp["q"].numpy(), ctx - 1, c, s)
+    assert _bits_equal(qd, qr)
+    rows = [0, 77, 128, 255]
+    o_ref = attn_decode_ref(qr[rows], inp["k_pool"].numpy(), inp["v_pool"].numpy(),
+                            inp["block_table"].numpy()[rows], ctx[rows], inp["scale"])
+    err = max_abs(of.float().cpu().numpy()[rows], o_ref)
+    print(f"paged_decode with rope: O {err:.2e}", flush=True)
+    assert err <= O_TOL
