@@ -277,6 +277,26 @@ def bench_rope(attn, W, dev, iters):
                                              **kw))
     t_att_r = timed(lambda: attn.prefill_paged(qp, kp, vp, bt, ctx, cq, pre["scale"], o=o,
                                                lse=lse, rope=tab, **kw))
+    # The rollout decode with the query rotation fused in, beside the plain
+    # decode (the pools' keys count as rotated; the timing does not depend on it).
+    dinp = W.decode_workload_inputs(DECODE_WORKLOAD)
+    dq_, dkp, dvp, dbt, dctx = (dinp[n].to(dev) for n in ("q", "k_pool", "v_pool", "block_table",
+                                                          "ctx_lens"))
+    dmc = int(dinp["ctx_lens"].max())
+    dtab = attn.rope_tables(dmc, d, 1e6, device=dev)
+    dout_ = torch.empty_like(dq_)
+    dws = torch.empty(max(1, attn.decode_workspace_bytes(attn.paged_dims(dq_, dkp, dbt, dmc))),
+                      dtype=torch.uint8, device=dev)
+    dvars = {"decode_us": lambda: attn.decode_paged(dq_, dkp, dvp, dbt, dctx, dinp["scale"],
+                                                    o=dout_, max_ctx_len=dmc, workspace=dws),
+             "decode_rope_us": lambda: attn.decode_paged(dq_, dkp, dvp, dbt, dctx, dinp["scale"],
+                                                         o=dout_, max_ctx_len=dmc, workspace=dws,
+                                                         rope=dtab)}
+    dbest = {name: float("inf") for name in dvars}
+    for _ in range(3):
+        for name, fn in dvars.items():
+            dbest[name] = min(dbest[name], timed(fn))
+    out.update({name: round(t * 1e6, 2) for name, t in dbest.items()})
     out.update({"prefill_workload": "paged_prefill",
                 "append_us": round(t_app * 1e6, 2), "append_rope_us": round(t_app_r * 1e6, 2),
                 "prefill_us": round(t_att * 1e6, 2), "prefill_rope_us": round(t_att_r * 1e6, 2)})
