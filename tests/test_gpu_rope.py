@@ -85,6 +85,12 @@ def test_rope_chunk_positions_bitwise(gpu):
     torch.cuda.synchronize()
     assert _bits_equal(q, rope_fp16_ref(inp["q"].numpy(), pos, c, s))
     assert _bits_equal(k, rope_fp16_ref(inp["k_new"].numpy(), pos, c, s))
+    # And back, at the same positions.
+    qi = q.clone()
+    attn.rope(qi, None, inp["cu_q"].to(gpu), tab, ctx_lens=inp["ctx_lens"].to(gpu),
+              max_ctx_len=inp["max_ctx"], max_seqlen=inp["max_q_len"], inverse=True)
+    torch.cuda.synchronize()
+    assert _bits_equal(qi, rope_fp16_ref(q.cpu().numpy(), pos, c, s, inverse=True))
 
 
 PRIOR = [0, 0, 5, 15, 16, 17, 100, 300, 0, 1000, 64, 511, 3, 31]
@@ -198,7 +204,9 @@ def test_rope_workload_bitwise(gpu):
     assert _bits_equal(k, rope_fp16_ref(inp["k"].numpy(), pos, c, s))
 
 
-def test_decode_step_with_rope(gpu):
+@pytest.mark.parametrize("h_q,h_kv,d", [(16, 8, 128), (8, 2, 64), (6, 6, 64)],
+                         ids=lambda x: str(x))
+def test_decode_step_with_rope(gpu, h_q, h_kv, d):
     """One rollout decode step with RoPE: attn_kv_append_rope stores the new
     token's rotated key, attn_rope (ctx_lens) rotates its query, and
     attn_decode_paged attends; attn_decode_paged_rope (rotating the query at
@@ -207,9 +215,9 @@ def test_decode_step_with_rope(gpu):
     the oracle decode over the oracle-rotated tensors."""
     from oracle import attn_decode_ref
     prior = [0, 15, 16, 100, 1000, 2047]
-    inp = W.make_prefill_inputs(prior, [1] * len(prior), 16, 8, 128, seed=6400)
+    inp = W.make_prefill_inputs(prior, [1] * len(prior), h_q, h_kv, d, seed=6400 + d + h_q)
     pos = chunk_positions(inp["cu_q"].numpy(), inp["ctx_lens"].numpy())
-    (c, s), tab = _tables(inp["max_ctx"], 128, gpu)
+    (c, s), tab = _tables(inp["max_ctx"], d, gpu)
     dd = {k: (v.to(gpu) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     kw = dict(max_ctx_len=inp["max_ctx"], max_q_len=1)
     attn.kv_append(dd["k_new"], dd["v_new"], dd["cu_q"], dd["block_table"], dd["ctx_lens"],
