@@ -127,12 +127,44 @@ def test_rope_oracle_pin(pin):
     pin(R)
 
 
-def test_rope_fp16_is_round_to_nearest():
-    x = np.array([[[1.0, 2.0]]])
-    cos, sin = R.rope_tables_ref(2, 2, 10.0)
-    y = R.rope_fp16_ref(x, [1], cos, sin)
+def pin_fp16_single_rounding(orc):
+    """rope_fp16_ref rounds the exact rotation to fp16 once, to nearest even.
+    Hand-derived values (fp16 has 10 fraction bits, spacing 2^-10 on [1, 2),
+    smallest subnormal 2^-24):
+      * position 0 is the identity, so the fp64 input itself is rounded:
+        1 + 2^-11 + 2^-40 lies just above the midpoint of 1 and 1 + 2^-10 and
+        gives 1 + 2^-10; 1 + 2^-11 - 2^-40 lies just below it and gives 1;
+        1 + 2^-11 exactly is a tie and goes to the even neighbour 1;
+        1 + 3 * 2^-11 is a tie between 1 + 2^-10 and 1 + 2^-9 and goes to
+        1 + 2^-9; 2^-25 + 2^-60 passes half the smallest subnormal and gives
+        2^-24, 2^-25 - 2^-60 gives 0;
+      * with cos = 0, sin = 1 (a quarter turn, given as explicit tables) the
+        pair (a, b) becomes (-b, a), and the rounding acts on the rotated
+        value: b = 1 + 2^-11 + 2^-40 gives -(1 + 2^-10) in slot 0.
+    Rounding through fp32 first (a plausible mistake) drops the 2^-40 and
+    2^-60 terms and turns the first and fifth cases into ties."""
+    e = 2.0 ** -40
+    vals = [1 + 2 ** -11 + e, 1 + 2 ** -11 - e, 1 + 2 ** -11, 1 + 3 * 2 ** -11,
+            2 ** -25 + 2 ** -60, 2 ** -25 - 2 ** -60]
+    want = [1 + 2 ** -10, 1.0, 1.0, 1 + 2 ** -9, 2 ** -24, 0.0]
+    cos, sin = orc.rope_tables_ref(1, 2 * len(vals), 10000.0)
+    x = np.array(vals + [0.0] * len(vals), dtype=np.float64)[None, None, :]
+    y = orc.rope_fp16_ref(x, [0], cos, sin)
     assert y.dtype == np.float16
-    np.testing.assert_array_equal(y, R.rope_ref(x, [1], cos, sin).astype(np.float16))
+    np.testing.assert_array_equal(y[0, 0, :len(vals)].astype(np.float64), want)
+    np.testing.assert_array_equal(y[0, 0, len(vals):].astype(np.float64), 0.0)
+    quarter_c = np.array([[1.0], [0.0]])
+    quarter_s = np.array([[0.0], [1.0]])
+    xq = np.array([[[1 + 2 ** -11 - e, 1 + 2 ** -11 + e]]])
+    yq = orc.rope_fp16_ref(xq, [1], quarter_c, quarter_s)
+    np.testing.assert_array_equal(yq[0, 0].astype(np.float64), [-(1 + 2 ** -10), 1.0])
+    # The inverse quarter turn maps (a, b) to (b, -a).
+    yi = orc.rope_fp16_ref(xq, [1], quarter_c, quarter_s, inverse=True)
+    np.testing.assert_array_equal(yi[0, 0].astype(np.float64), [1 + 2 ** -10, -1.0])
+
+
+def test_rope_fp16_is_round_to_nearest():
+    pin_fp16_single_rounding(R)
 
 
 # Planted mistakes.
@@ -165,6 +197,17 @@ def _rope_wrong_sign(x, pos, cos, sin, inverse=False):
     return _orig_rope(x, pos, cos, sin, not inverse)
 
 
+def _rope_fp16_via_fp32(x, pos, cos, sin, inverse=False):
+    return R.rope_ref(x, pos, cos, sin, inverse).astype(np.float32).astype(np.float16)
+
+
+def _rope_fp16_truncating(x, pos, cos, sin, inverse=False):
+    y = R.rope_ref(x, pos, cos, sin, inverse)
+    r = y.astype(np.float16)
+    over = np.abs(r.astype(np.float64)) > np.abs(y)
+    return np.where(over, np.nextafter(r, np.float16(0)), r).astype(np.float16)
+
+
 def _rope_off_by_one(x, pos, cos, sin, inverse=False):
     return _orig_rope(x, np.asarray(pos) + 1, np.vstack([cos, cos[-1:]]),
                       np.vstack([sin, sin[-1:]]), inverse)
@@ -180,6 +223,8 @@ MUTANTS = [
     ("rope_ref", _rope_wrong_sign, [pin_complex_form, pin_worked_example,
                                     pin_transformers_qwen3]),
     ("rope_ref", _rope_off_by_one, [pin_complex_form, pin_worked_example, pin_orthogonal]),
+    ("rope_fp16_ref", _rope_fp16_via_fp32, [pin_fp16_single_rounding]),
+    ("rope_fp16_ref", _rope_fp16_truncating, [pin_fp16_single_rounding]),
 ]
 
 
