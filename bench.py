@@ -2,17 +2,23 @@
 """Benchmark of the causal GQA attention hot path on one MI355X.
 
 One step = one pass over every stage of the path on resident synthetic
-inputs: attn_fwd + attn_bwd on the Qwen3-0.6B training workload (B=8,
-S=1024, H_q=16, H_kv=8, d=128, fp16) and attn_decode_paged on the rollout
-decode workload (256 sequences, ctx U{128..4096}, 16-token blocks).
+inputs: attn_fwd + attn_bwd on the long-context training workload (B=4,
+S=8192, H_q=16, H_kv=8, d=128, fp16; the largest training workload that one
+GPU holds) and attn_decode_paged on the rollout decode workload (256
+sequences, ctx U{128..4096}, 16-token blocks).
 
 Prints ONE JSON line. ``value`` is the forward+backward attention
 throughput in TFLOP/s (causal FLOP count: 4*d*H_q per unmasked (query, key)
 pair for the forward, 2.5x that for the backward) from HIP events on the
 launch stream; the decode bandwidth (algorithmic bytes / event time) rides
-along in ``decode``. ``roofline`` reports the kernel that takes the most time
+along in ``decode``. ``configs`` holds every workload: the tiny case (µs),
+the 1024-token, GRPO varlen and long-context training batches (fwd and bwd
+µs as median / min / max of per-launch event times, TFLOP/s on the median
+and its fraction of the dense fp16 MFMA peak) and the decode (GB/s, fraction
+of HBM peak). ``roofline`` reports the entry point that takes the most time
 per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same training workload. ``prefill`` times the rollout
+bounded sample of the long-context workload, with the host's CPU model,
+core counts and BLAS library. ``prefill`` times the rollout
 engine's chunked prefill (attn_kv_append + attn_prefill_paged on the
 paged_prefill workload) separately, after the timed steps; it is not part of
 ``value``. ``measured_peaks`` holds this GPU's measured dense fp16 MFMA rate,
@@ -40,8 +46,9 @@ sys.path.insert(0, ROOT)
 
 MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk, dense fp16
 HBM_PEAK_GBPS = 8000.0
-TRAIN_WORKLOAD = "qwen3_train"
+TRAIN_WORKLOAD = "long_context"
 DECODE_WORKLOAD = "paged_decode"
+ROPE_WORKLOAD = "qwen3_train"
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_cache.hip",
                   "attn_norm.hip", "attn_sample.hip", "attn_rope.hip", "probe_peaks.hip", "cdna4.h",
                   "kernels.h", "attn_api.cpp"]
@@ -84,10 +91,11 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of entry point `kernel` on `workload` from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -98,17 +106,41 @@ def read_traffic(kernel):
     return float(m_b.group(1))
 
 
+def host_facts():
+    """CPU model, logical CPUs, CPUs this process may run on, and the BLAS
+    library NumPy calls with its thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = []
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas.append({"library": i.get("internal_api"), "version": i.get("version"),
+                             "threads": i.get("num_threads"),
+                             "arch": i.get("architecture")})
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def cpu_baseline(budget_s):
     """The fp64 oracle (as it stands) on whole (sequence, KV-group) slices of the
-    training workload, forward + backward, until `budget_s` seconds pass."""
-    import numpy as np
+    long-context workload, forward + backward, until `budget_s` seconds pass
+    (at least one slice)."""
     from causal_gqa_attention_fa2_amd import workloads as W
     from oracle import attn_bwd_ref, attn_fwd_ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    facts = host_facts()
+    threads = max([b["threads"] or 1 for b in facts["blas"]] or [1])
     inp = W.workload_inputs(TRAIN_WORKLOAD)
     cu = inp["cu_seqlens"].tolist()
     G = inp["h_q"] // inp["h_kv"]
@@ -116,7 +148,7 @@ def cpu_baseline(budget_s):
     n = 0
     slices = [(b, g) for b in range(len(cu) - 1) for g in range(inp["h_kv"])]
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:  # whole passes over the slices, then stop
+    while n == 0 or time.perf_counter() - t0 < budget_s:  # whole slices, then stop
         for b, g in slices:
             s, e = cu[b], cu[b + 1]
             hs = slice(g * G, (g + 1) * G)
@@ -134,8 +166,9 @@ def cpu_baseline(budget_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} (sequence, KV-group) slices of {TRAIN_WORKLOAD} "
-                      f"({len(slices)} per batch), fwd+bwd in fp64, {dt:.1f} s wall",
-            "seconds": dt}
+                      f"({len(slices)} per batch: one sequence, its 2 query heads and 1 KV "
+                      f"head), fwd+bwd in fp64, {dt:.1f} s wall",
+            "host": facts, "seconds": dt}
 
 
 PREFILL_WORKLOAD = "paged_prefill"
@@ -201,7 +234,7 @@ def bench_rope(attn, W, dev, iters):
     attn_bwd alone; and on the paged_prefill workload the append and the
     prefill with the rotation fused in, beside the same calls without it."""
     import torch
-    inp = W.workload_inputs(TRAIN_WORKLOAD, with_dout=False)
+    inp = W.workload_inputs(ROPE_WORKLOAD, with_dout=False)
     q, k, cu = inp["q"].to(dev), inp["k"].to(dev), inp["cu_seqlens"].to(dev)
     T, h_q, d = q.shape
     h_kv = k.shape[1]
@@ -225,7 +258,7 @@ def bench_rope(attn, W, dev, iters):
     t_i = timed(lambda: attn.rope(q, k, cu, tab, max_seqlen=ms, inverse=True))
     # q and k read and written once, one table row (cos and sin) per token.
     nbytes = 2 * T * (h_q + h_kv) * d * 2 + T * d * 4
-    out = {"workload": f"{TRAIN_WORKLOAD} q+k ({T} tokens, H_q={h_q}, H_kv={h_kv}, d={d})",
+    out = {"workload": f"{ROPE_WORKLOAD} q+k ({T} tokens, H_q={h_q}, H_kv={h_kv}, d={d})",
            "fwd_us": round(t_f * 1e6, 2), "fwd_GB/s": round(nbytes / t_f / 1e9, 1),
            "inv_us": round(t_i * 1e6, 2), "inv_GB/s": round(nbytes / t_i / 1e9, 1),
            "fwd_hbm_peak_frac": round(nbytes / t_f / 1e9 / HBM_PEAK_GBPS, 4)}
@@ -233,7 +266,7 @@ def bench_rope(attn, W, dev, iters):
     # Training step on the rotated q and k: attn_bwd_rope (inverse rotation of
     # dq, dk fused into the stores) against attn_bwd with and without the
     # separate inverse pass.
-    tr_v = W.workload_inputs(TRAIN_WORKLOAD)
+    tr_v = W.workload_inputs(ROPE_WORKLOAD)
     v, dout = tr_v["v"].to(dev), tr_v["dout"].to(dev)
     o, lse = attn.fwd(q, k, v, cu, inp["scale"], max_seqlen=ms)
     dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
@@ -437,6 +470,101 @@ def measured_peaks(dev):
                    "16-byte non-temporal reads of 2 GiB, 8 in flight per thread; best of 3"}
 
 
+def _stats(ts):
+    """Median / min / max of per-launch times (seconds) in µs."""
+    xs = sorted(ts)
+    return {"median": round(xs[len(xs) // 2] * 1e6, 2), "min": round(xs[0] * 1e6, 2),
+            "max": round(xs[-1] * 1e6, 2)}
+
+
+def _rate(alg, ts, peak, scale):
+    """Algorithmic work per launch over the median launch time, and its
+    fraction of `peak` (`scale` converts to the unit of `peak`)."""
+    xs = sorted(ts)
+    r = alg / xs[len(xs) // 2] / scale
+    return round(r, 2), round(r / peak, 4)
+
+
+class TrainCase:
+    """Resident inputs, outputs and workspace of one training workload, with
+    the forward and backward as calls that allocate nothing."""
+
+    def __init__(self, attn, W, name, dev):
+        import torch
+        self.name = name
+        self.inp = W.workload_inputs(name)
+        q, k, v, dout = (self.inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+        cu = self.inp["cu_seqlens"].to(dev)
+        T, h_q, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((h_q, T), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ms, sc = self.inp["max_seqlen"], self.inp["scale"]
+        ws = torch.empty(max(attn.bwd_workspace_bytes(attn.varlen_dims(q, k, cu, ms)), 1),
+                         dtype=torch.uint8, device=dev)
+        self.fwd = lambda: attn.fwd(q, k, v, cu, sc, o=o, lse=lse, max_seqlen=ms)
+        self.bwd = lambda: attn.bwd(q, k, v, o, lse, dout, cu, sc, dq=dq, dk=dk, dv=dv,
+                                    max_seqlen=ms, workspace=ws)
+        self.costs = train_costs(self.inp)
+
+
+class DecodeCase:
+    def __init__(self, attn, W, name, dev):
+        import torch
+        self.inp = de = W.decode_workload_inputs(name)
+        q, kp, vp, bt, ctx = (de[n].to(dev) for n in ("q", "k_pool", "v_pool", "block_table",
+                                                      "ctx_lens"))
+        od = torch.empty_like(q)
+        pdims = attn.paged_dims(q, kp, bt, de["max_ctx"])
+        wsd = torch.empty(max(attn.decode_workspace_bytes(pdims), 1), dtype=torch.uint8,
+                          device=dev)
+        self.run = lambda: attn.decode_paged(q, kp, vp, bt, ctx, de["scale"], o=od,
+                                             max_ctx_len=de["max_ctx"], workspace=wsd)
+        self.costs = decode_costs(de)
+
+
+def time_launches(fns, iters, warm=2):
+    """Per-launch event times (seconds) of each function in `fns`, launched in
+    turn `iters` times back to back on the current stream, with one event
+    between consecutive launches. Returns one list per function."""
+    import torch
+    for _ in range(warm):
+        for f in fns:
+            f()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters * len(fns) + 1)]
+    ev[0].record()
+    i = 0
+    for _ in range(iters):
+        for f in fns:
+            f()
+            i += 1
+            ev[i].record()
+    ev[-1].synchronize()
+    out = [[] for _ in fns]
+    for j in range(iters * len(fns)):
+        out[j % len(fns)].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    return out
+
+
+def train_entry(case, t_fwd, t_bwd, with_rates=True):
+    """Per-config object: fwd and bwd µs (median / min / max), TFLOP/s on the
+    median and its fraction of the dense fp16 MFMA peak; fwd+bwd likewise."""
+    f_fwd, f_bwd, b_fwd, b_bwd = case.costs
+    e = {"fwd_us": _stats(t_fwd), "bwd_us": _stats(t_bwd),
+         "tokens": case.inp["total_tokens"], "max_seqlen": case.inp["max_seqlen"]}
+    if with_rates:
+        for nm, alg, ts in (("fwd", f_fwd, t_fwd), ("bwd", f_bwd, t_bwd)):
+            r, fr = _rate(alg, ts, MFMA_F16_PEAK_TFLOPS, 1e12)
+            e[f"{nm}_TFLOP/s"] = r
+            e[f"{nm}_mfma_peak_frac"] = fr
+        tot = [a + b for a, b in zip(t_fwd, t_bwd)]
+        r, fr = _rate(f_fwd + f_bwd, tot, MFMA_F16_PEAK_TFLOPS, 1e12)
+        e["fwd+bwd_TFLOP/s"] = r
+        e["fwd+bwd_mfma_peak_frac"] = fr
+        e["fwd_hbm_GB/s"] = round(b_fwd / sorted(t_fwd)[len(t_fwd) // 2] / 1e9, 1)
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +574,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peak probes (MFMA rate, streaming read)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the step (long_context fwd+bwd, paged_decode) and the "
+                         "per-config training rows; skip prefill, RMSNorm, sampling, RoPE")
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="untimed steady-state run before the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -472,35 +603,19 @@ def main():
     from causal_gqa_attention_fa2_amd import workloads as W
 
     dev = torch.device("cuda:0")
-    tr = W.workload_inputs(TRAIN_WORKLOAD)
-    de = W.decode_workload_inputs(DECODE_WORKLOAD)
-    q, k, v, dout = (tr[n].to(dev) for n in ("q", "k", "v", "dout"))
-    cu = tr["cu_seqlens"].to(dev)
-    T, h_q, d = q.shape
-    o = torch.empty_like(q)
-    lse = torch.empty((h_q, T), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    vd = attn.varlen_dims(q, k, cu, tr["max_seqlen"])
-    ws = torch.empty(max(attn.bwd_workspace_bytes(vd), 1), dtype=torch.uint8, device=dev)
-    dq_, kp, vp, bt, ctx = (de[n].to(dev) for n in ("q", "k_pool", "v_pool", "block_table",
-                                                    "ctx_lens"))
-    od = torch.empty_like(dq_)
-    pdims = attn.paged_dims(dq_, kp, bt, de["max_ctx"])
-    wsd = torch.empty(max(attn.decode_workspace_bytes(pdims), 1), dtype=torch.uint8, device=dev)
-    scale = tr["scale"]
+    tr = TrainCase(attn, W, TRAIN_WORKLOAD, dev)
+    dc = DecodeCase(attn, W, DECODE_WORKLOAD, dev)
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        attn.fwd(q, k, v, cu, scale, o=o, lse=lse, max_seqlen=tr["max_seqlen"])
+        tr.fwd()
         if ev:
             ev[1].record()
-        attn.bwd(q, k, v, o, lse, dout, cu, scale, dq=dq, dk=dk, dv=dv,
-                 max_seqlen=tr["max_seqlen"], workspace=ws)
+        tr.bwd()
         if ev:
             ev[2].record()
-        attn.decode_paged(dq_, kp, vp, bt, ctx, de["scale"], o=od, max_ctx_len=de["max_ctx"],
-                          workspace=wsd)
+        dc.run()
         if ev:
             ev[3].record()
 
@@ -520,28 +635,52 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
-    t_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
-    t_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+    ts_fwd = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
+    ts_bwd = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+    ts_dec = [e[2].elapsed_time(e[3]) * 1e-3 for e in evs]
+    t_fwd = sum(ts_fwd) / args.steps
+    t_bwd = sum(ts_bwd) / args.steps
+    t_dec = sum(ts_dec) / args.steps
 
-    f_fwd, f_bwd, b_fwd, b_bwd = train_costs(tr)
-    f_dec, b_dec = decode_costs(de)
+    f_fwd, f_bwd, b_fwd, b_bwd = tr.costs
+    f_dec, b_dec = dc.costs
     tflops = (f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12
     dec_gbps = b_dec / t_dec / 1e9
 
     parts = {
         "attn_fwd": dict(t=t_fwd, bound="mfma", achieved=f_fwd / t_fwd / 1e12,
-                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_fwd),
+                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_fwd,
+                         launches=["fwd_kernel<128, false, false>"]),
         "attn_bwd": dict(t=t_bwd, bound="mfma", achieved=f_bwd / t_bwd / 1e12,
-                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_bwd),
+                         peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_bwd,
+                         launches=["dq_kernel<128, false>", "dkdv_kernel<128, false, false>"]),
         "attn_decode_paged": dict(t=t_dec, bound="hbm", achieved=dec_gbps, peak=HBM_PEAK_GBPS,
-                                  unit="GB/s", alg=b_dec),
+                                  unit="GB/s", alg=b_dec,
+                                  launches=["decode_plan_kernel", "decode_gather_kernel<128, 2>",
+                                            "decode_combine_kernel<128>"]),
     }
     dom = max(parts, key=lambda n: parts[n]["t"])
     p = parts[dom]
-    roofline = {"kernel": dom, "bound": p["bound"], "achieved": round(p["achieved"], 2),
-                "peak": p["peak"], "unit": p["unit"], "frac": round(p["achieved"] / p["peak"], 4),
-                "traffic": read_traffic(dom)}
+    wl = DECODE_WORKLOAD if dom == "attn_decode_paged" else TRAIN_WORKLOAD
+    roofline = {"kernel": dom, "workload": wl, "launches": p["launches"], "bound": p["bound"],
+                "achieved": round(p["achieved"], 2), "peak": p["peak"], "unit": p["unit"],
+                "frac": round(p["achieved"] / p["peak"], 4),
+                "avg_launch_us": round(p["t"] * 1e6, 2),
+                "traffic": read_traffic(dom, wl)}
+
+    configs = {"long_context": train_entry(tr, ts_fwd, ts_bwd)}
+    configs["long_context"]["source"] = "the timed steps"
+    for name in ("tiny", "qwen3_train", "grpo_varlen"):
+        c = TrainCase(attn, W, name, dev)
+        tf, tb = time_launches([c.fwd, c.bwd], max(args.steps, 20))
+        configs[name] = train_entry(c, tf, tb, with_rates=name != "tiny")
+        del c
+    configs[DECODE_WORKLOAD] = {"us": _stats(ts_dec), "GB/s": round(b_dec / sorted(ts_dec)[
+        len(ts_dec) // 2] / 1e9, 1), "hbm_peak_frac": round(b_dec / sorted(ts_dec)[
+            len(ts_dec) // 2] / 1e9 / HBM_PEAK_GBPS, 4), "alg_bytes": int(b_dec),
+        "source": "the timed steps"}
+    order = ["tiny", "qwen3_train", "grpo_varlen", "long_context", DECODE_WORKLOAD]
+    configs = {k: configs[k] for k in order}
 
     out = {
         "metric": "attn fwd+bwd TFLOP/s & % FP16 MFMA peak; paged-decode HBM GB/s",
@@ -557,10 +696,10 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": "qwen3_train fwd+bwd (B=8, S=1024, H_q=16, H_kv=8, d=128, causal) + "
+            "workload": "long_context fwd+bwd (B=4, S=8192, H_q=16, H_kv=8, d=128, causal) + "
                         "paged_decode (256 seqs, ctx U{128..4096}, block 16, H_q=16, H_kv=8, "
                         "d=128)",
-            "global_batch": 8, "seq_len": 1024, "parallelism": "single-gpu",
+            "global_batch": 4, "seq_len": 8192, "parallelism": "single-gpu",
         },
         "mfma_peak_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "fwd": {"us": round(t_fwd * 1e6, 2), "TFLOP/s": round(parts["attn_fwd"]["achieved"], 2),
@@ -571,6 +710,7 @@ def main():
                    "hbm_peak_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "alg_bytes": int(b_dec), "launches": 3},
         "roofline": roofline,
+        "configs": configs,
         "source_digest": source_digest(),
     }
     peaks = None if args.no_peaks else measured_peaks(dev)
@@ -578,10 +718,11 @@ def main():
         out["measured_peaks"] = peaks
         out["mfma_measured_frac"] = round(tflops / peaks["mfma_f16_tflops"], 4)
         out["decode"]["hbm_measured_frac"] = round(dec_gbps / peaks["stream_read_gbps"], 4)
-    out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
-    out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
-    out["sampling"] = bench_sampling(attn, W, dev, max(args.steps, 5))
-    out["rope"] = bench_rope(attn, W, dev, max(args.steps, 5))
+    if not args.no_extras:
+        out["prefill"] = bench_prefill(attn, W, dev, max(args.steps, 5))
+        out["rmsnorm"] = bench_rmsnorm(attn, W, dev, max(args.steps, 5))
+        out["sampling"] = bench_sampling(attn, W, dev, max(args.steps, 5))
+        out["rope"] = bench_rope(attn, W, dev, max(args.steps, 5))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.cpu_budget)
         cb.pop("seconds", None)

@@ -79,6 +79,9 @@ attn_status check_paged(const attn_paged_dims* d, bool* empty) {
   if (d->block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (d->n_seqs > 65535 || d->h_kv > 65535) return ATTN_ERR_UNSUPPORTED;  // grid y/z limits
   if ((int64_t)d->max_blocks_per_seq * 16 < d->max_ctx_len) return ATTN_ERR_INVALID_ARG;
+  // Block counts and their prefix sums are int32 on the device.
+  if ((int64_t)d->n_seqs * (((int64_t)d->max_ctx_len + 15) / 16) > (INT32_MAX >> 1))
+    return ATTN_ERR_UNSUPPORTED;
   *empty = d->n_seqs == 0;
   // A non-empty context needs at least one pool block.
   if (!*empty && d->max_ctx_len > 0 && d->num_blocks == 0) return ATTN_ERR_INVALID_ARG;
@@ -293,6 +296,8 @@ static attn_status decode_impl(const attn_paged_dims* dims, const void* q, const
   a.head_dim = dims->head_dim;
   a.max_blocks_per_seq = dims->max_blocks_per_seq;
   a.n_wgs = cgqa::decode_num_wgs(dims->n_seqs, dims->max_ctx_len);
+  a.num_blocks = dims->num_blocks;
+  a.max_ctx_len = dims->max_ctx_len;
   a.scale = scale;
   if (rope) {
     a.rope_cos = rope->cos;

@@ -51,6 +51,10 @@ struct DecParams {
   int32_t* __restrict__ blk_start;  // [n + 1]
   int32_t* __restrict__ wg_first;   // [n_wgs]
   int n, h_q, h_kv, G, max_blocks, n_wgs;
+  // Pool size and the largest context the table rows can address: every
+  // context length is clamped into [0, max_ctx] and every table entry into
+  // [0, num_blocks), so no access leaves the pools or the table rows.
+  int num_blocks, max_ctx;
   float scale_log2;
   // RoPE tables [max_pos, D / 2] to rotate each query by its position
   // ctx - 1 as it is loaded, or null.
@@ -75,6 +79,14 @@ __device__ __forceinline__ void merge_state(SoftState& s, float m2, float l2, co
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Context length of sequence b as every kernel of the decode uses it: the
+// caller's value clamped into [0, max_ctx] (max_ctx <= 16 * max_blocks, so
+// ceil(ctx / 16) table entries of the row exist). The plan, the gather and
+// the combine all see the same value, so the block ranges agree.
+__device__ __forceinline__ int ctx_of(const DecParams& p, int b) {
+  return min(max(p.ctx[b], 0), p.max_ctx);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecParams p) 
   int carry = 0;
   for (int base = 0; base < p.n; base += kPlanThreads) {
     const int b = base + tid;
-    const int nb = b < p.n ? ceil_div(p.ctx[b], 16) : 0;
+    const int nb = b < p.n ? ceil_div(ctx_of(p, b), 16) : 0;
     int x = nb;  // inclusive scan over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecParams p) 
   // work-groups whose range starts inside sequence b.
   for (int b = tid; b < p.n; b += kPlanThreads) {
     const int start = p.blk_start[b];
-    const int nb = ceil_div(p.ctx[b], 16);
+    const int nb = ceil_div(ctx_of(p, b), 16);
     for (int w = ceil_div(start, chunk); w * chunk < start + nb; ++w) p.wg_first[w] = b;
   }
 }
@@ -165,7 +177,7 @@ __device__ __forceinline__ void gather_segment(const DecParams& p, int b, int g,
   constexpr int NTOK = NB * NLD;  // tokens per lane per iteration
   const int rg = lane / LPR;      // token row within a load instruction
   const int dc = lane % LPR;      // 8-column chunk of the head dimension
-  const int t_end = p.ctx[b];
+  const int t_end = ctx_of(p, b);
 
   u32x4 qh[G];  // q chunk of each head as fp16 pairs
 #pragma unroll
@@ -209,7 +221,8 @@ __device__ __forceinline__ void gather_segment(const DecParams& p, int b, int g,
     // Table entries of the next (up to) 64 blocks, one per lane.
     const int cnt = min(64, j1 - win);
     int my_phys = 0;
-    if (lane < cnt) my_phys = table[win + lane];
+    // win + lane < j1 <= ceil(t_end / 16) <= max_blocks: inside the row.
+    if (lane < cnt) my_phys = min(max(table[win + lane], 0), p.num_blocks - 1);
     for (int i0 = 0; i0 < cnt; i0 += NB) {
       // Loads are unconditional (a guarded load lets the compiler reuse its
       // destination register and wait on it before issuing the next one):
@@ -441,6 +454,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.G = a.h_q / a.h_kv;
   p.max_blocks = a.max_blocks_per_seq;
   p.n_wgs = a.n_wgs;
+  p.num_blocks = a.num_blocks;
+  p.max_ctx = a.max_ctx_len;
   p.scale_log2 = a.scale * kLog2e;
   p.cos_t = a.rope_cos;
   p.sin_t = a.rope_sin;

@@ -105,6 +105,10 @@ struct DecodeArgs {
   float* part_ml;  // workspace: fp32 [n_wgs + n, h_q, 2] partial (max, sum)
   int32_t* plan;   // workspace: int32 [n + 1] block prefix sums, [n_wgs] first sequences
   int n_seqs, h_q, h_kv, head_dim, max_blocks_per_seq, n_wgs;
+  // Pool blocks and the largest context (<= 16 * max_blocks_per_seq): the
+  // kernels clamp contexts into [0, max_ctx_len] and table entries into
+  // [0, num_blocks).
+  int num_blocks = 0, max_ctx_len = 0;
   float scale;
   // RoPE tables [rope_max_pos, head_dim / 2] to rotate each query by its
   // position ctx - 1 as it is loaded, or null.

@@ -160,6 +160,12 @@ size_t attn_decode_workspace_bytes(const attn_paged_dims* dims);
  * Position t of sequence b is slot t % 16 of block block_table[b][t / 16].
  * Blocks past ceil(ctx/16) are never read; slots past the context inside the
  * last block may be read but never influence o (even if they hold NaN).
+ * Contents of ctx_lens and block_table are not validated (attn_check_paged
+ * does that on host copies), but a context outside [0, max_ctx_len] is
+ * clamped into it and a table entry outside [0, num_blocks) into that range,
+ * so no access leaves the pools or the table rows (o is then undefined).
+ * Returns ATTN_ERR_UNSUPPORTED when n_seqs * ceil(max_ctx_len / 16) exceeds
+ * 2^30 (the device's block counts are int32).
  */
 attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const void* k_pool,
                               const void* v_pool, const int32_t* block_table,

@@ -269,3 +269,29 @@ def test_decode_block_permutation_gpu(gpu):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     check_decode("decode permuted", inp, o1)
+
+
+def test_decode_clamps_bad_indices(gpu):
+    """Contexts outside [0, max_ctx_len] and table entries outside
+    [0, num_blocks) are clamped inside the kernels: the output equals, bit for
+    bit, the decode of the clamped (valid) inputs, which matches the oracle.
+    The index math was checked on the CPU first (every access in bounds)."""
+    inp = W.make_decode_inputs([300, 40, 700, 64], 16, 8, 128, seed=2700, max_blocks=50,
+                               spare_blocks=2)
+    nb = inp["num_blocks"]
+    max_ctx = 800  # 50 blocks of 16
+    bad_ctx = torch.tensor([300, -5, 900, 64], dtype=torch.int32)
+    bad_bt = inp["block_table"].clone()
+    bad_bt[0, 2] = -7
+    bad_bt[0, 5] = nb + 3
+    bad_bt[3, 1] = 2 ** 31 - 1
+    good_ctx = torch.tensor([300, 0, 800, 64], dtype=torch.int32)
+    good_bt = bad_bt.clamp(0, nb - 1)
+    good = dict(inp, ctx_lens=good_ctx, block_table=good_bt, max_ctx=max_ctx)
+    bad = dict(inp, ctx_lens=bad_ctx, block_table=bad_bt, max_ctx=max_ctx)
+    o_bad = gpu_decode(dev(bad, gpu))
+    o_good = gpu_decode(dev(good, gpu))
+    torch.cuda.synchronize()
+    assert torch.equal(o_bad, o_good)
+    assert torch.equal(o_bad[1].cpu(), torch.zeros(16, 128, dtype=torch.float16))
+    check_decode("decode clamped", good, o_good)
