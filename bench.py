@@ -202,17 +202,9 @@ def bench_prefill(attn, W, dev, iters):
         attn.prefill_paged(q, kp, vp, bt, ctx, cu, inp["scale"], o=o, lse=lse, **kw)
 
     def timed(fn):
-        """Average time of `iters` back-to-back launches (HIP events on the
-        launch stream around the whole run)."""
-        for _ in range(3):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(iters):
-            fn()
-        ev[1].record()
-        ev[1].synchronize()
-        return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+        """Mean time of `iters` back-to-back launches, queued behind a spin
+        kernel so that the GPU never waits for the host."""
+        return sum(time_launches([fn], iters)[0]) / iters
 
     t_app = timed(append)  # rewrites the same slots: idempotent
     t_att = timed(prefill)
@@ -243,15 +235,9 @@ def bench_rope(attn, W, dev, iters):
     tab = attn.rope_tables(max_pos, d, 1e6, device=dev)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(iters):
-            fn()
-        ev[1].record()
-        ev[1].synchronize()
-        return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+        """Mean time of `iters` back-to-back launches, queued behind a spin
+        kernel so that the GPU never waits for the host."""
+        return sum(time_launches([fn], iters)[0]) / iters
 
     ms = inp["max_seqlen"]
     t_f = timed(lambda: attn.rope(q, k, cu, tab, max_seqlen=ms))
@@ -361,15 +347,9 @@ def bench_rmsnorm(attn, W, dev, iters):
                          dtype=torch.uint8, device=dev)
 
         def timed(fn):
-            for _ in range(3):
-                fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record()
-            for _ in range(iters):
-                fn()
-            ev[1].record()
-            ev[1].synchronize()
-            return ev[0].elapsed_time(ev[1]) / iters * 1e-3
+            """Mean time of `iters` back-to-back launches, queued behind a spin
+            kernel so that the GPU never waits for the host."""
+            return sum(time_launches([fn], iters)[0]) / iters
 
         t_f = timed(lambda: attn.rmsnorm_fwd(x, w, inp["eps"], y=y, rstd=rstd))
         t_b = timed(lambda: attn.rmsnorm_bwd(x, w, rstd, dy, dx=dx, dw=dw, workspace=ws))
@@ -523,15 +503,25 @@ class DecodeCase:
         self.costs = decode_costs(de)
 
 
+# Length of the spin kernel that the timed launches queue behind (shader
+# clock cycles, tens of milliseconds): longer than the host needs to enqueue
+# them, so the GPU runs them back to back instead of waiting for each call.
+SPIN_CYCLES = 60_000_000
+
+
 def time_launches(fns, iters, warm=2):
     """Per-launch event times (seconds) of each function in `fns`, launched in
     turn `iters` times back to back on the current stream, with one event
-    between consecutive launches. Returns one list per function."""
+    between consecutive launches. Everything is queued behind a spin kernel,
+    so the events time the GPU work and not the host's launch overhead.
+    Returns one list per function."""
     import torch
     for _ in range(warm):
         for f in fns:
             f()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters * len(fns) + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
     ev[0].record()
     i = 0
     for _ in range(iters):
