@@ -7,9 +7,10 @@ as hand-written HIP kernels behind the C ABI declared in include/attn.h.
 ``fwd``, ``bwd``, ``decode_paged``, ``kv_append`` and ``prefill_paged`` are
 thin ctypes wrappers of attn_fwd, attn_bwd, attn_decode_paged,
 attn_kv_append and attn_prefill_paged; the shared library is loaded on first
-use and every call raises if it is missing. ``rmsnorm_fwd`` / ``rmsnorm_bwd``
-wrap attn_rmsnorm_fwd / attn_rmsnorm_bwd, the layer normalisation next to
-attention. ``rope_tables`` / ``rope`` wrap attn_rope_tables_init / attn_rope
+use and every call raises if it is missing. ``decode_paged_noalloc`` wraps
+attn_decode_paged_noalloc, the decode for callers that cannot allocate.
+``rmsnorm_fwd`` / ``rmsnorm_bwd`` wrap attn_rmsnorm_fwd / attn_rmsnorm_bwd,
+the layer normalisation next to attention. ``rope_tables`` / ``rope`` wrap attn_rope_tables_init / attn_rope
 (rotary position embedding of q and k, and its inverse); ``kv_append`` and
 ``prefill_paged`` take ``rope=(cos, sin)`` to rotate inside those kernels.
 """
@@ -22,6 +23,7 @@ from .attn import (  # noqa: F401
     bwd,
     bwd_workspace_bytes,
     decode_paged,
+    decode_paged_noalloc,
     decode_workspace_bytes,
     fwd,
     kv_append,

@@ -24,7 +24,7 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_pag
             "attn_decode_workspace_bytes", "attn_kv_append", "attn_prefill_paged",
             "attn_rmsnorm_fwd", "attn_rmsnorm_bwd", "attn_rmsnorm_bwd_workspace_bytes",
             "attn_sample", "attn_rope_tables_init", "attn_rope", "attn_kv_append_rope", "attn_bwd_rope",
-            "attn_decode_paged_rope",
+            "attn_decode_paged_rope", "attn_decode_paged_noalloc",
             "attn_prefill_paged_rope",
             "attn_status_string", "attn_check_cu_seqlens", "attn_check_paged",
             "attn_check_prefill")
@@ -92,6 +92,9 @@ def load_library():
     lib.attn_decode_paged.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_float, _vp, ctypes.c_size_t, _vp]
     lib.attn_decode_paged.restype = ctypes.c_int
+    lib.attn_decode_paged_noalloc.argtypes = [ctypes.POINTER(PagedDims), _vp, _vp, _vp, _vp,
+                                              _vp, _vp, ctypes.c_float, _vp]
+    lib.attn_decode_paged_noalloc.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_check_cu_seqlens.argtypes = [ctypes.POINTER(VarlenDims), _vp]
@@ -332,6 +335,33 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_lens, scale=None, o=None,
            lib.attn_decode_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                  _ptr(block_table), _ptr(ctx_lens), _ptr(o), float(scale),
                                  _ptr(workspace), workspace.numel(), _stream()))
+    return o
+
+
+def decode_paged_noalloc(q, k_pool, v_pool, block_table, ctx_lens, o, max_ctx_len, scale=None):
+    """attn_decode_paged_noalloc: attn_decode_paged with the library's own
+    per-device workspace array, for callers that cannot allocate. The caller
+    passes the output o (fp16 [n, h_q, d]) and the host bound max_ctx_len;
+    nothing is allocated here or in the library. Returns o."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.float16, 3)
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    _need(o, "o", torch.float16, 3, dev)
+    n, h_q, d = q.shape
+    if k_pool.shape != v_pool.shape or k_pool.shape[3] != d or block_table.shape[0] != n or \
+            ctx_lens.shape[0] != n or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dims = paged_dims(q, k_pool, block_table, max_ctx_len)
+    _check("attn_decode_paged_noalloc",
+           lib.attn_decode_paged_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(block_table), _ptr(ctx_lens), _ptr(o),
+                                         float(scale), _stream()))
     return o
 
 

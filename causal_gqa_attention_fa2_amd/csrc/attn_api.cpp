@@ -261,21 +261,33 @@ size_t attn_decode_workspace_bytes(const attn_paged_dims* dims) {
   return decode_ws_parts(dims, &ob, &mb);
 }
 
+// Checks of a decode call's shape, tables and tensor pointers (all but the
+// workspace). Sets *empty when there is nothing to compute.
+static attn_status decode_check(const attn_paged_dims* dims, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table,
+                                const int32_t* ctx_lens, const attn_rope_tables* rope,
+                                const void* o, bool* empty) {
+  attn_status st = check_paged(dims, empty);
+  if (st != ATTN_OK) return st;
+  if (rope && (st = check_rope(rope, dims->max_ctx_len)) != ATTN_OK) return st;
+  if (*empty) return ATTN_OK;
+  if (!q || !ctx_lens || !o) return ATTN_ERR_INVALID_ARG;
+  if (dims->max_ctx_len > 0 && (!k_pool || !v_pool || !block_table)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
 static attn_status decode_impl(const attn_paged_dims* dims, const void* q, const void* k_pool,
                                const void* v_pool, const int32_t* block_table,
                                const int32_t* ctx_lens, const attn_rope_tables* rope, void* o,
                                float scale, void* workspace, size_t workspace_bytes,
                                void* stream) {
   bool empty = false;
-  attn_status st = check_paged(dims, &empty);
-  if (st != ATTN_OK) return st;
-  if (rope && (st = check_rope(rope, dims->max_ctx_len)) != ATTN_OK) return st;
-  if (empty) return ATTN_OK;
-  if (!q || !ctx_lens || !o) return ATTN_ERR_INVALID_ARG;
-  if (dims->max_ctx_len > 0 && (!k_pool || !v_pool || !block_table)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      ((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
-    return ATTN_ERR_INVALID_ARG;
+  const attn_status st =
+      decode_check(dims, q, k_pool, v_pool, block_table, ctx_lens, rope, o, &empty);
+  if (st != ATTN_OK || empty) return st;
   size_t ob, mb;
   const size_t need = decode_ws_parts(dims, &ob, &mb);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kWsAlign)))
@@ -313,6 +325,22 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
                               size_t workspace_bytes, void* stream) {
   return decode_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, nullptr, o, scale, workspace,
                      workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_noalloc(const attn_paged_dims* dims, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      void* o, float scale, void* stream) {
+  bool empty = false;
+  const attn_status st =
+      decode_check(dims, q, k_pool, v_pool, block_table, ctx_lens, nullptr, o, &empty);
+  if (st != ATTN_OK || empty) return st;
+  size_t ob, mb;
+  if (decode_ws_parts(dims, &ob, &mb) > cgqa::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (cgqa::decode_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  return decode_impl(dims, q, k_pool, v_pool, block_table, ctx_lens, nullptr, o, scale, ws,
+                     cgqa::kDecodeScratchBytes, stream);
 }
 
 attn_status attn_decode_paged_rope(const attn_paged_dims* dims, const void* q,

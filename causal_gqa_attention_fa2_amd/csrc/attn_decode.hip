@@ -32,6 +32,8 @@
 #include "cdna4.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace cgqa {
 namespace {
 
@@ -435,6 +437,34 @@ hipError_t launch_d(const DecParams& p, int G, hipStream_t stream) {
 }
 
 }  // namespace
+}  // namespace cgqa
+
+// Device array that stands in for the workspace of the allocation-free
+// decode. Host code never uses this name as an address: the runtime gives
+// each device's copy its own device address (decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[cgqa::kDecodeScratchBytes];
+
+namespace cgqa {
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   DecParams p;

@@ -126,6 +126,12 @@ inline int decode_num_wgs(int n_seqs, int max_ctx_len) {
   return bound < 1 ? 1 : (bound < kDecodeMaxWGs ? (int)bound : kDecodeMaxWGs);
 }
 
+// Workspace of the allocation-free decode: a device array of this many bytes
+// (one per device, held until the process ends). decode_scratch returns the
+// current device's copy, looked up on the first call on that device.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Query-stationary work-groups (forward and dQ) have kQWaves waves; each wave
 // owns 32 query rows of one head. A work-group covers hpw heads of a KV
 // group (hpw = the largest power of two <= min(G, kQWaves)) and

@@ -22,7 +22,9 @@
  *    16-byte aligned.
  *  - The caller owns every buffer (inputs, outputs, workspace). The library
  *    never allocates, frees or keeps a pointer after the call returns, never
- *    synchronizes and never copies device data to the host.
+ *    synchronizes and never copies device data to the host. The one
+ *    library-held buffer is the fixed device array of
+ *    attn_decode_paged_noalloc, part of the loaded code itself.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the null
  *    stream) and the call returns before it finishes. Calls are stateless and
  *    may be captured into a HIP graph.
@@ -171,6 +173,29 @@ attn_status attn_decode_paged(const attn_paged_dims* dims, const void* q, const 
                               const void* v_pool, const int32_t* block_table,
                               const int32_t* ctx_lens, void* o, float scale, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and checks as
+ * attn_decode_paged, minus the workspace: the work plan and the partials
+ * live in a 32 MiB (33554432-byte) device array that the library holds, one
+ * copy per device, from the first call on that device until the process
+ * ends. The call itself allocates nothing.
+ *   Returns ATTN_ERR_WORKSPACE, enqueuing nothing, when
+ *   attn_decode_workspace_bytes(dims) exceeds 33554432 bytes (e.g. more than
+ *   about 3500 sequences at h_q = 16, d = 128); ATTN_ERR_HIP if the device
+ *   array's address cannot be looked up.
+ *   Every call on one device shares that device's array and leaves its
+ *   partials there; nothing in it needs to start at zero. Calls that may run
+ *   at the same time on one device (different streams, or several host
+ *   threads each with its own stream) race on it and give undefined output;
+ *   calls on one stream are ordered and safe.
+ */
+attn_status attn_decode_paged_noalloc(const attn_paged_dims* dims, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      void* o, float scale, void* stream);
 
 /* Shape of a chunked prefill over a paged cache: `paged` describes the
  * pools, the block table and the contexts (ctx_lens count each sequence's

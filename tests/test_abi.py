@@ -130,6 +130,27 @@ def test_decode_argument_checks(lib):
     assert call(PagedDims(0, 16, 8, 128, 16, 256, 1000, 4096), ws=0, nbytes=0) == OK
 
 
+def test_decode_noalloc_argument_checks(lib):
+    """The allocation-free decode makes the decode's checks, then refuses a
+    batch whose workspace exceeds its 32 MiB device array, all before any
+    HIP call."""
+    p = ctypes.c_void_p
+
+    def call(d, q=FAKE, bt=FAKE):
+        return lib.attn_decode_paged_noalloc(ctypes.byref(d), p(q), p(FAKE), p(FAKE), p(bt),
+                                             p(FAKE), p(FAKE), 0.1, None)
+
+    big = PagedDims(4096, 16, 8, 128, 16, 1, 1, 16)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(big)) > (32 << 20)
+    assert call(big) == WORKSPACE
+    assert call(PagedDims(4, 16, 8, 128, 32, 256, 1000, 4096)) == UNSUPPORTED
+    assert call(PagedDims(4, 16, 8, 128, 16, 100, 1000, 4096)) == INVALID
+    assert call(PagedDims(4, 16, 8, 128, 16, 256, 1000, 4096), q=0) == INVALID
+    assert call(PagedDims(4, 16, 8, 128, 16, 256, 1000, 4096), bt=FAKE + 1) == INVALID
+    assert call(PagedDims(0, 16, 8, 128, 16, 256, 1000, 4096)) == OK
+    assert lib.attn_decode_paged_noalloc(None, *([p(FAKE)] * 6), 0.1, None) == INVALID
+
+
 def test_host_validators():
     dims = VarlenDims(3, 10, 7, 4, 2, 64)
     ok = torch.tensor([0, 3, 3, 10], dtype=torch.int32)
