@@ -53,8 +53,8 @@ attn_status check_varlen(const attn_varlen_dims* d, bool* empty) {
   return ATTN_OK;
 }
 
-// Workspace of the backward: two fp32 [h_q, T] row-term arrays, D =
-// rowsum(dO * O) and LSE * log2(e), each starting on a 256-byte boundary.
+// Workspace of the backward: two fp32 [h_q, T] row-term arrays, -D =
+// -rowsum(dO * O) and LSE * log2(e), each starting on a 256-byte boundary.
 size_t bwd_row_bytes(const attn_varlen_dims* d) {
   return align_up((size_t)d->h_q * d->total_tokens * sizeof(float));
 }

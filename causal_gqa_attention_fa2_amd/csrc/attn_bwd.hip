@@ -57,6 +57,10 @@ constexpr int kDqBC = 32;       // keys per K/V tile (dq kernel)
 constexpr int kDqStages = 3;    // K/V ring depth (dq kernel)
 constexpr int kKvStages = 4;    // Q/dO ring depth (dkdv kernel)
 constexpr int kBK = 128;        // keys per dkdv work-group (4 x 32)
+// Accumulator chains of dkdv's first product. One dependent chain measured
+// faster than two interleaved ones (which need 16 adds to merge): the other
+// wave of the SIMD keeps the matrix core busy between the chain's products.
+constexpr int kDkdvChains = 1;
 constexpr int kBwdThreads = 512;
 
 struct BwdParams {
@@ -67,7 +71,7 @@ struct BwdParams {
   const float* __restrict__ lse;
   const f16* __restrict__ dout;
   const int32_t* __restrict__ cu;
-  float* __restrict__ drow;  // workspace: fp32 [h_q, T], rowsum(dO * O)
+  float* __restrict__ drow;  // workspace: fp32 [h_q, T], -D = -rowsum(dO * O)
   float* __restrict__ lse2;  // workspace: fp32 [h_q, T], LSE * log2(e)
   f16* __restrict__ dq;
   f16* __restrict__ dk;
@@ -134,6 +138,24 @@ __device__ __forceinline__ void store_acc_row(f16* row, const f32x16* acc, float
         *(f16x4*)(row + 32 * db + 8 * r4 + 4 * hi) = w;
       }
     }
+  }
+}
+
+// dS = P * (dP - D) in fp16 for the 16 accumulator elements of a lane (dpd
+// holds dP - D), each product rounded once (v_fma_mix*_f16): elements
+// 8u .. 8u + 7 go to f[u].
+__device__ __forceinline__ void ds_pack(const float* pv, const f32x16& dpd, f16x8* f) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 8 * u + 2 * e;
+      const f16x2 r = {(f16)__builtin_fmaf(pv[i], dpd[i], 0.f),
+                       (f16)__builtin_fmaf(pv[i + 1], dpd[i + 1], 0.f)};
+      w[e] = __builtin_bit_cast(uint32_t, r);
+    }
+    f[u] = __builtin_bit_cast(f16x8, w);
   }
 }
 
@@ -214,16 +236,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   // lands in chunk slot l % CH of its row and fetches the global chunk the
   // swizzle maps there. Keys past the sequence fetch its last row (their
   // scores are masked).
+  // The tile's first row is a wave-uniform base in SGPRs; each lane adds a
+  // 32-bit byte offset fixed for the kernel, recomputed with the clamp only
+  // on the sequence's last tile.
+  const int tsel = (wave * CPW) / NI;  // K (waves 0-3) or V (4-7)
+  auto copy_off = [&](int c, int last) {
+    const int r = ((wave * CPW) % NI + c) * RPI + lane / CH;
+    return (uint32_t)(min(r, last) * p.h_kv * D + swz<D>(r, (lane % CH) * 8)) * 2u;
+  };
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue_tile = [&](const Item& it, int kt, int st) {
+    const int k0 = kt * kDqBC;
+    const f16* base = (tsel ? p.v : p.k) + ((size_t)(it.s0 + k0) * p.h_kv + it.g) * D;
+    const bool tail = k0 + kDqBC > it.L;  // wave-uniform
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int i = wave * CPW + c;
-      const int tsel = i / NI;
-      const int ii = i % NI;
-      const int r = ii * RPI + lane / CH;
-      const int sl = (lane % CH) * 8;
-      const size_t row = ((size_t)(it.s0 + min(kt * kDqBC + r, it.L - 1)) * p.h_kv + it.g) * D;
-      dma16((tsel ? p.v : p.k) + row + swz<D>(r, sl), smem + (2 * st + tsel) * TILE + ii * 512);
+      const int ii = (wave * CPW) % NI + c;
+      dma16s_at(base, copy_off(c, tail ? it.L - 1 - k0 : 31),
+                smem_lds + (uint32_t)((2 * st + tsel) * TILE + ii * 512) * 2u);
     }
   };
   // This wave's rows of item `it`: head hig of the group's chunk, 32 query
@@ -321,7 +351,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       const f16* Vb = Kb + TILE;
       // S^T and dP^T for the tile's 32 keys (accumulator element i: key
       // k0 + 8(i/4) + 4hi + i%4, query qpos), two interleaved chains.
-      f32x16 sv = zero_f32x16(), dp = zero_f32x16();
+      // dP^T starts from -D, so the chain yields dP^T - D.
+      f32x16 sv = zero_f32x16(), dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[i] = -dsum;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         sv = mfma32x32x16(*(const f16x8*)(Kb + koff[t]), qf[t], sv);
@@ -343,20 +376,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
         // Diagonal tile: keep P where key <= qpos, i.e. the constant part
         // 8(i/4) + i%4 of the key is <= qpos - k0 - 4hi.
         const int lim = rw.qpos - k0 - 4 * hi;
+        float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
-          if (8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
-          dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
+          pv[i] = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
+          if (8 * (i >> 2) + (i & 3) > lim) pv[i] = 0.f;
         }
+        ds_pack(pv, dp, dsf);
       } else {
         // Every other tile takes this unmasked copy (two copies, so the
         // compiler does not evaluate the mask everywhere).
+        float pv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
-          dsf[i >> 3][i & 7] = (f16)(pv * (dp[i] - dsum));
-        }
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(sv[i], p.scale_log2, -lse2));
+        ds_pack(pv, dp, dsf);
       }
       // dQ^T += K^T dS^T over the 32 keys (K^T by transpose reads).
 #pragma unroll
@@ -378,7 +411,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       f16* dqrow = p.dq + ((size_t)rw.qrow * p.h_q + rw.head) * D;
       store_acc_row<D, ROPE>(dqrow, acc, p.scale, hi, p, rw.qpos);
       if (hi == 0) {
-        p.drow[(size_t)rw.head * p.T + rw.qrow] = dsum;
+        p.drow[(size_t)rw.head * p.T + rw.qrow] = -dsum;
         p.lse2[(size_t)rw.head * p.T + rw.qrow] = lse2;
       }
     }
@@ -445,24 +478,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   const int n_qb = (L + 31) / 32 - qb_begin;
   const int n_it = p.G * n_qb;
 
-  // Copy of block m into stage st. Instruction i (of 2 * IPB) fills rows
-  // (i % IPB) * RPI + lane / CH of Q (i < IPB) or dO; wave 0 also copies the
-  // row terms. Rows past the sequence fetch its last row; the mask below
-  // zeroes their weights.
-  auto issue_blk = [&](int m, int st) {
-    if (team != 0) return;
+  // Copies of block m into stage st: team-0 wave w4 issues CPW of the block's
+  // 2 * IPB copy instructions, all of one tensor (Q for w4 < 2, dO after);
+  // instruction ii fills rows ii * RPI + lane / CH. The block's first row is
+  // a wave-uniform base in SGPRs and each lane adds a 32-bit offset fixed for
+  // the loop; on the sequence's last block rows past the end are clamped to
+  // its last row (the mask below zeroes their weights). Wave 0 also copies
+  // the row terms.
+  const int tsel = (w4 * CPW) / IPB;
+  // Byte offset of the lane's chunk of copy c in a block, and the same with
+  // its row clamped to `last`.
+  auto copy_off = [&](int c, int last) {
+    const int r = ((w4 * CPW) % IPB + c) * RPI + lane / CH;
+    return (uint32_t)(min(r, last) * p.h_q * D + swz<D>(r, (lane % CH) * 8)) * 2u;
+  };
+  uint32_t coff[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) coff[c] = copy_off(c, 31);
+  const uint32_t xs_lds = lds_addr(&Xs[0][0][0]);
+  auto issue_blk = [&](int m, auto ST) {
+    constexpr int st = decltype(ST)::value;
     const int head = g * p.G + m / n_qb;
     const int q0 = (qb_begin + m % n_qb) * 32;
+    const f16* base = (tsel ? p.dout : p.q) + ((size_t)(s0 + q0) * p.h_q + head) * D;
+    const bool tail = q0 + 31 >= L;  // wave-uniform
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int i = w4 * CPW + c;
-      const int tsel = i / IPB;
-      const int ii = i % IPB;
-      const int r = ii * RPI + lane / CH;
-      const int sl = (lane % CH) * 8;
-      const f16* src = (tsel ? p.dout : p.q) +
-                       ((size_t)(s0 + min(q0 + r, L - 1)) * p.h_q + head) * D + swz<D>(r, sl);
-      dma16(src, &Xs[st][tsel][ii * 512]);
+      const int ii = (w4 * CPW) % IPB + c;
+      dma16s_at(base, tail ? copy_off(c, L - 1 - q0) : coff[c],
+                xs_lds + (uint32_t)((st * 2 + tsel) * BLK + ii * 512) * 2u);
     }
     if (wave == 0) {
       const float* src = (lane < 32 ? p.lse2 : p.drow) + (size_t)head * p.T + s0 +
@@ -473,7 +517,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 
   // Block 0's copies go out before the ordinary loads below, so the two
   // latencies overlap.
-  issue_blk(0, 0);
+  if (team == 0) issue_blk(0, std::integral_constant<int, 0>{});
 
   // K (team 0) or V (team 1) of the pair's keys as the B operand: lane holds
   // row `key` (rows past the end read the last row; never stored), columns
@@ -485,10 +529,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     for (int t = 0; t < NT; ++t) kvf[t] = *(const f16x8*)(src + 16 * t);
   }
 
-  // Per-lane LDS offsets (halves) within a block, fixed for the loop.
+  // Per-lane LDS offsets (halves) within a block, fixed for the loop; the
+  // team's tile (X: rows of the first product; Y: transposed operand of the
+  // second) is folded in, so that with compile-time ring stages every read
+  // below is a per-lane register plus an immediate.
+  const int xsel = team * BLK, ysel = (1 - team) * BLK;
   int xoff[NT];  // row l32, columns 16t + 8hi (first GEMM's A operand)
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xoff[t] = l32 * D + swz<D>(l32, 16 * t + 8 * hi);
+  for (int t = 0; t < NT; ++t) xoff[t] = xsel + l32 * D + swz<D>(l32, 16 * t + 8 * hi);
   // Transpose reads of rows 16u + 4hi + j16/4 (and 8 further), columns
   // 32db + 16(grp&1) + 4(j16&3): A slot e of half hi <-> query row
   // 16u + 8(e/4) + 4hi + e%4, the slot order of the P / dS B operand.
@@ -498,9 +546,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     const int col = 32 * db + 16 * (grp & 1) + 4 * (j16 & 3);
     const int r0 = 4 * hi + (j16 >> 2);
     const int r1 = r0 + 8;
-    yoff0[db] = r0 * D + swz<D>(r0, col);
-    yoff1[db] = r1 * D + swz<D>(r1, col);
+    yoff0[db] = ysel + r0 * D + swz<D>(r0, col);
+    yoff1[db] = ysel + r1 * D + swz<D>(r1, col);
   }
+  const int loff = 32 * team + 4 * hi;  // row terms: LSE * log2(e) (team 0) or -D (team 1)
 
   f32x16 acc[ND];  // dV^T (team 0) or dK^T (team 1): rows = head dim, cols = keys
 #pragma unroll
@@ -521,72 +570,93 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     *(f16x8*)(dst + 8) = f[1];
   };
 
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): see dq_kernel
-  if (n_it > 1) issue_blk(1, 1);
-  for (int j = 0; j <= n_it; ++j) {
+  // Iteration j of team TEAM on the ring stage of its block (a compile-time
+  // constant: the loop below is unrolled by the ring depth, and j = J mod 4).
+  // Team 0 works on block j, team 1 on block j - 1.
+  auto body = [&](int j, auto J, auto TEAM) {
+    constexpr int tm = decltype(TEAM)::value;
     // Block j has landed for every wave (block j + 1 may still be in
     // flight), every wave is done with its block of the previous iteration,
     // and team 0's P of block j - 1 is in LDS.
-    if (team == 1) {
+    if constexpr (tm == 1) {
       lds_barrier();  // no copies of its own; its dS stores stay in flight
-    } else if (j + 1 < n_it) {
-      if (wave == 0) wait_vm_barrier<CPW + 1>();
-      else wait_vm_barrier<CPW>();
     } else {
-      wait_vm_barrier<0>();
+      if (j + 1 < n_it) {
+        if (wave == 0) wait_vm_barrier<CPW + 1>();
+        else wait_vm_barrier<CPW>();
+      } else {
+        wait_vm_barrier<0>();
+      }
+      // Stage (j + 2) % 4 last held block j - 2, which team 1 finished in
+      // the previous iteration.
+      if (j + 2 < n_it)
+        issue_blk(j + 2, std::integral_constant<int, (decltype(J)::value + 2) % kKvStages>{});
     }
-    // Stage (j + 2) % 4 last held block j - 2, which team 1 finished in the
-    // previous iteration.
-    if (j + 2 < n_it) issue_blk(j + 2, (j + 2) % kKvStages);
-    const int m = j - team;
-    if (m < 0 || m >= n_it) continue;  // uniform over the wave
-    const int st = m % kKvStages;
+    const int m = j - tm;
+    if (m < 0 || m >= n_it) return;  // uniform over the wave
+    constexpr int st = (decltype(J)::value - tm + kKvStages) % kKvStages;
+    constexpr int par = (decltype(J)::value - tm + kKvStages) & 1;  // m & 1
     const int q0 = (qb_begin + m % n_qb) * 32;
-    const f16* X = Xs[st][team];      // rows: Q (team 0) or dO (team 1)
-    const f16* Y = Xs[st][1 - team];  // transposed: dO (team 0) or Q (team 1)
+    const f16* Xb = &Xs[st][0][0];
 
     // Operand reads are issued in blocks ahead of their uses (scheduling
     // fences keep the compiler from sinking them): the row fragments of the
-    // first product, then, behind its matrix work, the transposed fragments
-    // of the second, the row terms and the P hand-off.
+    // first product (and team 1's row terms, its accumulator's start), then,
+    // behind its matrix work, the transposed fragments of the second, team
+    // 0's row terms and the P hand-off.
     f16x8 xfr[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) xfr[t] = *(const f16x8*)(X + xoff[t]);
-    __builtin_amdgcn_sched_barrier(0);
-    // S = Q K^T (team 0) or dP = dO V^T (team 1); accumulator element i:
-    // query row q0 + 8(i/4) + 4hi + i%4, key `key`.
-    // Two interleaved chains over even / odd k-steps (a single dependent
-    // chain would leave the matrix core idle between products).
-    f32x16 sa = zero_f32x16(), sb = zero_f32x16();
+    for (int t = 0; t < NT; ++t) xfr[t] = *(const f16x8*)(Xb + xoff[t]);
+    const float* lrow = &Ls[st][loff];
+    f32x4 l4[4];
+    if constexpr (tm == 1) {
 #pragma unroll
-    for (int t = 0; t < NT; t += 2) {
-      sa = mfma32x32x16(xfr[t], kvf[t], sa);
-      sb = mfma32x32x16(xfr[t + 1], kvf[t + 1], sb);
+      for (int jj = 0; jj < 4; ++jj) l4[jj] = *(const f32x4*)(lrow + 8 * jj);
     }
     __builtin_amdgcn_sched_barrier(0);
-    sa += sb;
+    // S = Q K^T (team 0) or dP - D = dO V^T - D (team 1, started from -D);
+    // accumulator element i: query row q0 + 8(i/4) + 4hi + i%4, key `key`.
+    // One chain over the k-steps, or two interleaved over even / odd ones
+    // (kDkdvChains).
+    f32x16 sa, sb = zero_f32x16();
+    if constexpr (tm == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[i] = l4[i >> 2][i & 3];
+    } else {
+      sa = zero_f32x16();
+    }
+    if constexpr (kDkdvChains == 2) {
+#pragma unroll
+      for (int t = 0; t < NT; t += 2) {
+        sa = mfma32x32x16(xfr[t], kvf[t], sa);
+        sb = mfma32x32x16(xfr[t + 1], kvf[t + 1], sb);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sa = mfma32x32x16(xfr[t], kvf[t], sa);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f16x8 yfr[ND][2];
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        yfr[db][u] = cat4(lds_read_tr(Y + yoff0[db] + 16 * u * D),
-                          lds_read_tr(Y + yoff1[db] + 16 * u * D));
+        yfr[db][u] = cat4(lds_read_tr(Xb + yoff0[db] + 16 * u * D),
+                          lds_read_tr(Xb + yoff1[db] + 16 * u * D));
     }
-    // Row terms of the same rows: 4 groups of 4 consecutive rows.
-    const float* lrow = &Ls[st][32 * team + 4 * hi];
-    f32x4 l4[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) l4[jj] = *(const f32x4*)(lrow + 8 * jj);
-    f16* px = &Px[m & 1][w4][lane * 8];
+    f16* px = &Px[par][w4][lane * 8];
     f16x8 p0, p1;
-    if (team == 1) {
+    if constexpr (tm == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) l4[jj] = *(const f32x4*)(lrow + 8 * jj);
+    } else {
       p0 = *(const f16x8*)px;
       p1 = *(const f16x8*)(px + 512);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kDkdvChains == 2) sa += sb;
     f16x8 f[2];
-    if (team == 0) {
+    if constexpr (tm == 0) {
       // Causal mask on diagonal blocks, row mask on the sequence's last
       // block; every other block takes the unmasked copy of the loop (two
       // copies, so the compiler does not evaluate the mask everywhere).
@@ -609,10 +679,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
       *(f16x8*)px = f[0];
       *(f16x8*)(px + 512) = f[1];
     } else {
+      // dS = P * (dP - D), one rounding to fp16 per element (the product of
+      // an fp16 and an fp32 value, rounded once: v_fma_mix).
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
-        f[i >> 3][i & 7] = (f16)(pv * (sa[i] - l4[i >> 2][i & 3]));
+      for (int u = 0; u < 2; ++u) {
+        const f16x8 pp = u ? p1 : p0;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 r = {(f16)__builtin_fmaf((float)pp[2 * e], sa[8 * u + 2 * e], 0.f),
+                           (f16)__builtin_fmaf((float)pp[2 * e + 1], sa[8 * u + 2 * e + 1], 0.f)};
+          w[e] = __builtin_bit_cast(uint32_t, r);
+        }
+        f[u] = __builtin_bit_cast(f16x8, w);
       }
       if constexpr (STORE_DS) store_ds(m, f);
     }
@@ -625,6 +704,29 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
       for (int db = 0; db < ND; ++db) acc[db] = mfma32x32x16(yfr[db][u], f[u], acc[db]);
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): see dq_kernel
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  static_assert(kKvStages == 4, "the loop is unrolled by the ring depth");
+  if (team == 0) {
+    if (n_it > 1) issue_blk(1, I1{});
+    for (int j = 0; j <= n_it; j += 4) {
+      body(j, I0{}, I0{});
+      if (j + 1 <= n_it) body(j + 1, I1{}, I0{});
+      if (j + 2 <= n_it) body(j + 2, I2{}, I0{});
+      if (j + 3 <= n_it) body(j + 3, I3{}, I0{});
+    }
+  } else {
+    for (int j = 0; j <= n_it; j += 4) {
+      body(j, I0{}, I1{});
+      if (j + 1 <= n_it) body(j + 1, I1{}, I1{});
+      if (j + 2 <= n_it) body(j + 2, I2{}, I1{});
+      if (j + 3 <= n_it) body(j + 3, I3{}, I1{});
+    }
   }
 
   if (key >= L) return;
@@ -636,8 +738,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 }
 
 
-// Row terms of the backward for every (token, query head) row: D = rowsum(dO
-// * O) and LSE * log2(e), stored [h_q, T]. A group of D/8 lanes owns a row.
+// Row terms of the backward for every (token, query head) row: -D =
+// -rowsum(dO * O) and LSE * log2(e), stored [h_q, T]. A group of D/8 lanes owns a row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
   constexpr int LPR = D / 8;
@@ -670,7 +772,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
         const int t = row / p.h_q;
         const int h = row - t * p.h_q;
         const size_t i = (size_t)h * p.T + t;
-        p.drow[i] = acc;
+        p.drow[i] = -acc;
         p.lse2[i] = p.lse[i] * kLog2e;
       }
     }

@@ -27,6 +27,7 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_raw __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -125,6 +126,21 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, f16* ld
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
                "s"(sbase)
                : "memory", "m0");
+}
+
+// dma16s with the LDS destination given as a wave-uniform byte address in
+// the LDS aperture (lds_addr(...) of a __shared__ object plus an offset), so
+// no generic pointer is formed.
+__device__ __forceinline__ void dma16s_at(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// Byte address of a __shared__ object in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // 4-byte-per-lane variant (global_load_lds_dword): lane l's dword lands at

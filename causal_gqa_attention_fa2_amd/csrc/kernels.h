@@ -81,7 +81,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* drow;    // workspace: fp32 [h_q, T], rowsum(dO * O)
+  float* drow;    // workspace: fp32 [h_q, T], -rowsum(dO * O)
   float* lse2;    // workspace: fp32 [h_q, T], LSE * log2(e)
   void* ds = nullptr;  // workspace: fp16 dS blocks (the dS path), or null
   // RoPE tables [rope_max_pos, head_dim / 2] to rotate dq and dk back with at

@@ -111,7 +111,7 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
                      float* lse, void* stream);
 
 /* Bytes of device workspace attn_bwd needs for `dims` (0 for an empty
- * batch). Holds two fp32 [h_q, T] arrays of per-row terms: D = rowsum(dO * O)
+ * batch). Holds two fp32 [h_q, T] arrays of per-row terms: -D = -rowsum(dO * O)
  * and LSE * log2(e). For batches of very unequal lengths (n_seqs >= 2 and
  * n_seqs * max_seqlen >= 1.25 total_tokens) it also holds fp16 dS blocks,
  * n_seqs * h_q * ceil(max_seqlen / 32)^2 * 2 KiB (when that is at most
