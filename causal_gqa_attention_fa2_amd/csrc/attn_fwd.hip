@@ -141,25 +141,47 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   // instruction lie in one 16-token block (RPI divides 16), so its physical
   // block is one wave-uniform scalar load; out-of-range table entries are
   // clamped into the pool, so no access leaves it.
-  auto issue_tile = [&](int kt, int stage) {
+  // Packed keys and values: the tile's first row is a wave-uniform base in
+  // SGPRs and each lane adds a 32-bit byte offset fixed for the kernel
+  // (recomputed with the clamp only on the sequence's last tile).
+  auto copy_off = [&](int i, int last, bool tr) {
+    const int r = (wave * IPW + i) * RPI + lane / CH;
+    const int col = tr ? swz_tr<D>(r, (lane % CH) * 8) : swz<D>(r, (lane % CH) * 8);
+    return (uint32_t)(min(r, last) * p.h_kv * D + col) * 2u;
+  };
+  uint32_t koffc[IPW], voffc[IPW];
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int r = (wave * IPW + i) * RPI + lane / CH;
-      const int slot = (lane % CH) * 8;
-      size_t row;
-      if constexpr (PAGED) {
+  for (int i = 0; i < IPW; ++i) {
+    koffc[i] = copy_off(i, kBC - 1, false);
+    voffc[i] = copy_off(i, kBC - 1, true);
+  }
+  const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
+  auto issue_tile = [&](int kt, int stage) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int r = (wave * IPW + i) * RPI + lane / CH;
+        const int slot = (lane % CH) * 8;
         const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
         const int lb = min(t0 >> 4, p.max_blocks - 1);
         const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
         const int t = min(kt * kBC + r, Lk - 1);
-        row = ((size_t)(phys * 16 + (t - (lb << 4))) * p.h_kv + g) * D;
-      } else {
-        row = ((size_t)(s0 + min(kt * kBC + r, L - 1)) * p.h_kv + g) * D;
+        const size_t row = ((size_t)(phys * 16 + (t - (lb << 4))) * p.h_kv + g) * D;
+        f16* kdst = Ks[stage] + (wave * IPW + i) * 64 * 8;
+        f16* vdst = Vs[stage] + (wave * IPW + i) * 64 * 8;
+        dma16(p.k + row + swz<D>(r, slot), kdst);
+        dma16(p.v + row + swz_tr<D>(r, slot), vdst);
       }
-      f16* kdst = Ks[stage] + (wave * IPW + i) * 64 * 8;
-      f16* vdst = Vs[stage] + (wave * IPW + i) * 64 * 8;
-      dma16(p.k + row + swz<D>(r, slot), kdst);
-      dma16(p.v + row + swz_tr<D>(r, slot), vdst);
+    } else {
+      const int k0 = kt * kBC;
+      const size_t base = ((size_t)(s0 + k0) * p.h_kv + g) * D;
+      const bool tail = k0 + kBC > L;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+        dma16s_at(p.k + base, tail ? copy_off(i, L - 1 - k0, false) : koffc[i], ks_lds + dst);
+        dma16s_at(p.v + base, tail ? copy_off(i, L - 1 - k0, true) : voffc[i], vs_lds + dst);
+      }
     }
   };
 
@@ -259,9 +281,14 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
         }
       }
     }
-    float mx = fmaxf(s[0][0], s[1][0]);
+    // Two independent three-input max chains (v_max3_f32) over the 32 scores.
+    float mx0 = fmaxf(s[0][0], s[1][0]), mx1 = fmaxf(s[0][1], s[1][1]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    for (int i = 2; i < 16; i += 2) {
+      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][i]), s[1][i]);
+      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[0][i + 1]), s[1][i + 1]);
+    }
+    float mx = fmaxf(mx0, mx1);
     mx = half_swap_max(mx) * p.scale_log2;
     // m_run is a reference point, not always the exact running maximum: it
     // moves (and O and l are rescaled) only when a row's maximum passes it by
