@@ -13,7 +13,9 @@ pair for the forward, 2.5x that for the backward) from HIP events on the
 launch stream; the decode bandwidth (algorithmic bytes / event time) rides
 along in ``decode``. ``configs`` holds every workload: the tiny case (µs),
 the 1024-token, GRPO varlen and long-context training batches (fwd and bwd
-µs as median / min / max of per-launch event times, TFLOP/s on the median
+µs as median / min / max: over the timed steps for long_context, else over
+5 groups of 20 back-to-back launches, each group timed by one event pair;
+TFLOP/s on the median
 and its fraction of the dense fp16 MFMA peak) and the decode (GB/s, fraction
 of HBM peak). ``roofline`` reports the entry point that takes the most time
 per step against its bound; ``cpu_baseline`` times the fp64 CPU oracle on a
@@ -204,7 +206,7 @@ def bench_prefill(attn, W, dev, iters):
     def timed(fn):
         """Mean time of `iters` back-to-back launches, queued behind a spin
         kernel so that the GPU never waits for the host."""
-        return sum(time_launches([fn], iters)[0]) / iters
+        return time_launches([fn], iters)[0][0]
 
     t_app = timed(append)  # rewrites the same slots: idempotent
     t_att = timed(prefill)
@@ -237,7 +239,7 @@ def bench_rope(attn, W, dev, iters):
     def timed(fn):
         """Mean time of `iters` back-to-back launches, queued behind a spin
         kernel so that the GPU never waits for the host."""
-        return sum(time_launches([fn], iters)[0]) / iters
+        return time_launches([fn], iters)[0][0]
 
     ms = inp["max_seqlen"]
     t_f = timed(lambda: attn.rope(q, k, cu, tab, max_seqlen=ms))
@@ -349,7 +351,7 @@ def bench_rmsnorm(attn, W, dev, iters):
         def timed(fn):
             """Mean time of `iters` back-to-back launches, queued behind a spin
             kernel so that the GPU never waits for the host."""
-            return sum(time_launches([fn], iters)[0]) / iters
+            return time_launches([fn], iters)[0][0]
 
         t_f = timed(lambda: attn.rmsnorm_fwd(x, w, inp["eps"], y=y, rstd=rstd))
         t_b = timed(lambda: attn.rmsnorm_bwd(x, w, rstd, dy, dx=dx, dw=dw, workspace=ws))
@@ -451,7 +453,7 @@ def measured_peaks(dev):
 
 
 def _stats(ts):
-    """Median / min / max of per-launch times (seconds) in µs."""
+    """Median / min / max of launch-time samples (seconds) in µs."""
     xs = sorted(ts)
     return {"median": round(xs[len(xs) // 2] * 1e6, 2), "min": round(xs[0] * 1e6, 2),
             "max": round(xs[-1] * 1e6, 2)}
@@ -507,33 +509,35 @@ class DecodeCase:
 # clock cycles, tens of milliseconds): longer than the host needs to enqueue
 # them, so the GPU runs them back to back instead of waiting for each call.
 SPIN_CYCLES = 60_000_000
+# Samples (groups of back-to-back launches) behind each per-config median / min / max.
+CONFIG_REPS = 5
 
 
-def time_launches(fns, iters, warm=2):
-    """Per-launch event times (seconds) of each function in `fns`, launched in
-    turn `iters` times back to back on the current stream, with one event
-    between consecutive launches. Everything is queued behind a spin kernel,
-    so the events time the GPU work and not the host's launch overhead.
-    Returns one list per function."""
+def time_launches(fns, iters, reps=1, warm=2):
+    """Mean launch time (seconds) of each function in `fns`: `reps` samples per
+    function, each one event pair around `iters` back-to-back launches of it
+    (the functions take turns, group by group). Everything is queued behind a
+    spin kernel, so the events time the GPU work and not the host's launch
+    overhead, and no event sits between two launches of a group (an event
+    between kernels adds the drain of one before the next starts, several µs).
+    Returns one list of `reps` samples per function."""
     import torch
     for _ in range(warm):
         for f in fns:
             f()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters * len(fns) + 1)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(reps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(SPIN_CYCLES)
-    ev[0].record()
-    i = 0
-    for _ in range(iters):
-        for f in fns:
-            f()
-            i += 1
-            ev[i].record()
-    ev[-1].synchronize()
-    out = [[] for _ in fns]
-    for j in range(iters * len(fns)):
-        out[j % len(fns)].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
-    return out
+    for r in range(reps):
+        for fi, f in enumerate(fns):
+            ev[r][fi][0].record()
+            for _ in range(iters):
+                f()
+            ev[r][fi][1].record()
+    ev[-1][-1][1].synchronize()
+    return [[ev[r][fi][0].elapsed_time(ev[r][fi][1]) * 1e-3 / iters for r in range(reps)]
+            for fi in range(len(fns))]
 
 
 def train_entry(case, t_fwd, t_bwd, with_rates=True):
@@ -662,7 +666,7 @@ def main():
     configs["long_context"]["source"] = "the timed steps"
     for name in ("tiny", "qwen3_train", "grpo_varlen"):
         c = TrainCase(attn, W, name, dev)
-        tf, tb = time_launches([c.fwd, c.bwd], max(args.steps, 20))
+        tf, tb = time_launches([c.fwd, c.bwd], max(args.steps, 20), reps=CONFIG_REPS)
         configs[name] = train_entry(c, tf, tb, with_rates=name != "tiny")
         del c
     configs[DECODE_WORKLOAD] = {"us": _stats(ts_dec), "GB/s": round(b_dec / sorted(ts_dec)[
