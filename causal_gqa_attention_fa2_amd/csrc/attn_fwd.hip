@@ -38,6 +38,7 @@
 #include "cdna4.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 
@@ -66,8 +67,73 @@ struct FwdParams {
   const float* __restrict__ sin_t;
   int max_pos;
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles;
+  // Ragged batches: 1 when work-groups walk the list of non-empty query tiles
+  // (varlen_item) instead of every (query tile, sequence) slot.
+  int mapped;
   float scale_log2;  // scale * log2(e)
 };
+
+// Largest batch the query-tile list handles: n_seqs <= kMapSeqs, and the
+// host also bounds n_seqs * ceil(n_qtiles / 64) (the cost of the list).
+constexpr int kMapChunks = 4;
+constexpr int kMapSeqs = 64 * kMapChunks;
+
+// Item k of the heaviest-first list of the batch's query tiles: the pairs
+// (sequence b, query tile qt) with qt * BR < L_b, ordered by qt descending
+// (the tiles with the most keys first), then by b. Every wave of the
+// work-group computes the same answer from cu_seqlens; lane l handles the
+// sequences l + 64c. Returns false when k is past the end of the list.
+//   nt_b = ceil(L_b / BR) (at most n_qtiles), A(t) = sum_b max(nt_b - t, 0)
+//   is the number of items with tile index >= t, so item k has the largest
+//   qt with A(qt) > k, and is the (k - A(qt + 1))-th sequence with nt_b > qt.
+__device__ __forceinline__ bool varlen_item(const FwdParams& p, int k, int lane, int BR, int& qt,
+                                            int& b) {
+  int nt[kMapChunks];
+#pragma unroll
+  for (int c = 0; c < kMapChunks; ++c) {
+    const int bb = lane + 64 * c;
+    nt[c] = 0;
+    if (bb < p.n_seqs) nt[c] = min((p.cu[bb + 1] - p.cu[bb] + BR - 1) / BR, p.n_qtiles);
+  }
+  // A(t) for t = lane + 64 j, by broadcasting each nt_b.
+  int cnt = 0;       // tiles t with A(t) > k
+  int a_next = 0;    // A(qt + 1), found below
+  const int nj = (p.n_qtiles + 63) >> 6;
+  for (int j = 0; j < nj; ++j) {
+    const int t = lane + 64 * j;
+    int a = 0;
+#pragma unroll
+    for (int c = 0; c < kMapChunks; ++c) {
+      if (64 * c >= p.n_seqs) break;  // uniform
+      const int nb = min(p.n_seqs - 64 * c, 64);
+      for (int i = 0; i < nb; ++i) a += max(__builtin_amdgcn_readlane(nt[c], i) - t, 0);
+    }
+    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < p.n_qtiles && a > k));
+    // A is non-increasing in t, so the tiles with A(t) > k are 0 .. cnt - 1;
+    // A(cnt) is this lane's value where t == cnt.
+    if (__builtin_amdgcn_ballot_w64(t == cnt)) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(t == cnt);
+      a_next = __builtin_amdgcn_readlane(a, __builtin_ctzll(m));
+    }
+  }
+  if (cnt == 0) return false;  // k >= A(0), the number of items
+  qt = cnt - 1;
+  int r = k - (qt + 1 < p.n_qtiles ? a_next : 0);
+#pragma unroll
+  for (int c = 0; c < kMapChunks; ++c) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(nt[c] > qt);
+    const int n = __builtin_popcountll(m);
+    if (r < n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint64_t sel = __builtin_amdgcn_ballot_w64(nt[c] > qt && below == r);
+      b = 64 * c + __builtin_ctzll(sel);
+      return true;
+    }
+    r -= n;
+  }
+  return false;
+}
 
 // PAGED = false: the packed varlen forward (keys and values of sequence b
 // are rows cu[b] .. cu[b+1]-1 of k and v; query i sits at position i).
@@ -93,17 +159,25 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
 
   const int BR = 32 * p.nqb;
   // Heaviest query tiles (the last ones of the longest sequences) first.
-  const int per = p.n_seqs * p.h_kv * p.n_chunks;
   // Work-group and lane ids come straight from the hardware registers: this
   // file is built without IEEE mode, so device-library helpers (compiled
   // with it) are not inlined here and none may be called.
   const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-  const int qt = p.n_qtiles - 1 - wg / per;
-  int rem = wg % per;
-  const int chunk = rem % p.n_chunks;
-  rem /= p.n_chunks;
-  const int g = rem % p.h_kv;
-  const int b = rem / p.h_kv;
+  const int hc = p.h_kv * p.n_chunks;
+  const int chunk = (wg % hc) % p.n_chunks;
+  const int g = (wg % hc) / p.n_chunks;
+  int qt, b;
+  if (p.mapped) {
+    // Ragged batch: work-group w takes item w / hc of the list of non-empty
+    // query tiles (work-groups past its end exit).
+    if (!varlen_item(p, wg / hc, (int)__builtin_amdgcn_workitem_id_x() & 63, BR, qt, b)) return;
+    qt = __builtin_amdgcn_readfirstlane(qt);
+    b = __builtin_amdgcn_readfirstlane(b);
+  } else {
+    // Every (query tile, sequence) slot, tile index descending.
+    qt = p.n_qtiles - 1 - wg / (p.n_seqs * hc);
+    b = (wg % (p.n_seqs * hc)) / hc;
+  }
   const int s0 = p.cu[b];
   const int L = p.cu[b + 1] - s0;  // queries of the sequence
   const int q_wg0 = qt * BR;
@@ -398,7 +472,14 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   const int BR = 32 * p.nqb;
   p.n_qtiles = (a.max_seqlen + BR - 1) / BR;
   p.scale_log2 = a.scale * kLog2e;
-  const dim3 grid(p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks);
+  // Ragged batches walk the list of non-empty query tiles: at most
+  // floor(T / BR) + n_seqs of them (each sequence adds at most one partial
+  // tile), against n_qtiles * n_seqs slots.
+  const long long slots = (long long)p.n_qtiles * a.n_seqs;
+  const long long items = std::min<long long>(slots, (long long)a.total_tokens / BR + a.n_seqs);
+  p.mapped = items < slots && a.n_seqs <= kMapSeqs &&
+             (long long)a.n_seqs * ((p.n_qtiles + 63) / 64) <= 512;
+  const dim3 grid((unsigned)((p.mapped ? items : slots) * a.h_kv * p.n_chunks));
   if (PAGED && a.rope_cos != nullptr) {
     if (a.head_dim == 128)
       hipLaunchKernelGGL((fwd_kernel<128, true, true>), grid, dim3(kNTH), 0, stream, p);
