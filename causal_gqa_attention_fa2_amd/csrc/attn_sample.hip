@@ -4,20 +4,21 @@
 //
 // One work-group of 1024 threads per row:
 //  1. radix select (11 + 11 + 10 bits of an order-preserving key of the fp32
-//     logit, one LDS histogram per pass) finds K*, the k-th largest key; the
-//     first digit streams the row, then (when they fit) the keys past that
-//     digit are copied to LDS and the rest of the selection runs there, so
-//     the row is read twice instead of four times;
+//     logit, one LDS histogram per pass) finds K*, the k-th largest key. A
+//     first read of the row bounds the first digit from below through the
+//     threads' maxima; a second copies the keys from that digit up to LDS
+//     (when they fit), and all three digits are selected on that copy, so
+//     the row is read twice and no pass adds every key into one histogram;
 //  2. the keys above K* are gathered (with the keys equal to K* when all of
 //     them are kept, the usual case; otherwise the lowest-index keys equal
 //     to K* follow, in tiles of 1024 in index order with ranks from wave
 //     ballots), so the kept set is the first k of the ranking "logit
 //     descending, index ascending"; the row is streamed with 16-byte loads;
 //  3. a bitonic sort in LDS puts the k candidates in ranking order;
-//  4. weights w_j = exp((v_j - v_0) / T); one thread forms the cumulative
-//     sums c_j in ranking order, keeps ranks 0..cut with
-//     cut = min{j : c_j >= top_p c_last}, and returns the token at rank
-//     min{j <= cut : c_j > u c_cut} for the row's uniform u.
+//  4. weights w_j = exp((v_j - v_0) / T); the cumulative sums c_j in
+//     ranking order (a wave scan for k <= 64, else one thread), ranks
+//     0..cut kept with cut = min{j : c_j >= top_p c_last}, and the token at
+//     rank min{j <= cut : c_j > u c_cut} for the row's uniform u.
 // Scaling by 1/T > 0 keeps the order, so the selection runs on raw logits.
 // The result is a deterministic function of the logits and u.
 #include <hip/hip_runtime.h>
@@ -30,6 +31,7 @@ namespace {
 constexpr int kSampleThreads = 1024;
 constexpr int kWaves = kSampleThreads / 64;
 constexpr int kCandidates = 4096;  // LDS copy of the keys past the first radix digit
+constexpr int kHead = 16384;       // least number of logits behind the first bound
 
 struct SampleParams {
   const float* __restrict__ logits;
@@ -108,14 +110,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   // Sets s_digit, s_above (keys with larger digits) and s_eq (keys with
   // this digit).
   auto find_digit = [&](uint32_t need) {
-    suf[tid] = hist[2 * tid] + hist[2 * tid + 1];
-    __syncthreads();
-    for (int off = 1; off < kSampleThreads; off <<= 1) {
-      const uint32_t add = tid + off < kSampleThreads ? suf[tid + off] : 0u;
-      __syncthreads();
-      suf[tid] += add;
-      __syncthreads();
+    // Suffix sums over the pairs: within each wave by lane shuffles, then
+    // the totals of the waves above.
+    uint32_t v = hist[2 * tid] + hist[2 * tid + 1];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(v, off, 64);
+      if (lane + off < 64) v += o;
     }
+    if (lane == 0) s_wave[wave] = v;
+    __syncthreads();
+    for (int w = wave + 1; w < kWaves; ++w) v += s_wave[w];
+    suf[tid] = v;
+    __syncthreads();
     const uint32_t above_pair = tid + 1 < kSampleThreads ? suf[tid + 1] : 0u;
     if (suf[tid] >= need && above_pair < need) {
       const uint32_t h1 = hist[2 * tid + 1];
@@ -143,29 +150,58 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   // whose first digit reaches the chosen one fit in LDS (kCandidates), one
   // more pass copies them there and the other digits (and the gather) work
   // on that copy instead of re-reading the row.
+  //
+  // A lower bound of the first digit comes without an LDS atomic per key:
+  // each thread's largest key over its share of the row, then the digit at
+  // which these 1024 maxima reach k. k threads hold a key in that digit or
+  // above, so the row's k-th largest key is there too. Every key from that
+  // digit up is then copied to LDS (a few hundred on language-model
+  // logits), and the first digit proper is counted on the copy, whose
+  // histogram above the bound is the row's.
+  // The maxima are taken over the row's first V0 logits only (about a
+  // sixteenth, and at least kHead or the whole row): the k-th largest key of
+  // a part of the row is a lower bound for the whole row's as well. The copy
+  // then reads the rest of the row and the first part again (just read, so
+  // mostly from cache): the row crosses HBM about once.
+  const int V0 = V <= kHead ? V : max(kHead, (V / 16 + 3) & ~3);
+  uint32_t tmax = 0;  // below every key: threads without logits count nothing
+  for_each_logit(row, V0, tid, [&](float x, int) { tmax = max(tmax, fkey(x)); });
   clear_hist();
-  for_each_logit(row, V, tid, [&](float x, int) { atomicAdd(&hist[fkey(x) >> 21], 1u); });
+  atomicAdd(&hist[tmax >> 21], 1u);
+  __syncthreads();
+  find_digit((uint32_t)p.k);
+  const uint32_t d0 = s_digit;
+  if (tid == 0) s_nb = 0;
+  __syncthreads();
+  auto copy_from = [&](int i0, int n) {
+    for_each_logit(row + i0, n, tid, [&](float x, int i) {
+      const uint32_t key = fkey(x);
+      if ((key >> 21) >= d0) {
+        const uint32_t slot = atomicAdd(&s_nb, 1u);
+        if (slot < (uint32_t)kCandidates) {
+          bkey[slot] = key;
+          bidx[slot] = i0 + i;
+        }
+      }
+    });
+  };
+  copy_from(V0, V - V0);
+  copy_from(0, V0);
+  __syncthreads();
+  const bool buffered = s_nb <= (uint32_t)kCandidates;  // uniform
+  const int nb = buffered ? (int)s_nb : 0;
+  clear_hist();
+  if (buffered) {
+    for (int j = tid; j < nb; j += kSampleThreads) atomicAdd(&hist[bkey[j] >> 21], 1u);
+  } else {
+    // More keys reach the bound than the copy holds: count the whole row.
+    for_each_logit(row, V, tid, [&](float x, int) { atomicAdd(&hist[fkey(x) >> 21], 1u); });
+  }
   __syncthreads();
   find_digit((uint32_t)p.k);
   uint32_t prefix = s_digit << 21;
   uint32_t need = (uint32_t)p.k - s_above;
-  const bool buffered = s_above + s_eq <= (uint32_t)kCandidates;  // uniform
   __syncthreads();
-  if (buffered) {
-    if (tid == 0) s_nb = 0;
-    __syncthreads();
-    const uint32_t d1 = prefix >> 21;
-    for_each_logit(row, V, tid, [&](float x, int i) {
-      const uint32_t key = fkey(x);
-      if ((key >> 21) >= d1) {
-        const uint32_t slot = atomicAdd(&s_nb, 1u);
-        bkey[slot] = key;
-        bidx[slot] = i;
-      }
-    });
-    __syncthreads();
-  }
-  const int nb = buffered ? (int)s_nb : 0;
 #pragma unroll 1
   for (int pass = 1; pass < 3; ++pass) {
     const int shift = pass == 1 ? 10 : 0;
@@ -246,8 +282,36 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   }
   __syncthreads();
 
-  // 3. Bitonic sort of the 1024 slots into ranking order.
-  for (int size = 2; size <= kSampleThreads; size <<= 1) {
+  // 3. Bitonic sort into ranking order: of the first 64 slots by one wave
+  // (lane shuffles, no barriers) when at most 64 are filled, else of all
+  // 1024 slots.
+  if (filled <= 64) {
+    if (wave == 0) {
+      float v = cval[lane];
+      int ix = cidx[lane];
+#pragma unroll
+      for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const float vo = __shfl_xor(v, stride, 64);
+          const int io = __shfl_xor(ix, stride, 64);
+          // The lower lane of a pair keeps the earlier element when the
+          // block sorts ascending in ranking order (lane & size == 0).
+          const bool lower = (lane & stride) == 0;
+          const bool up = (lane & size) == 0;
+          const bool mine_first = before(v, ix, vo, io);
+          if (mine_first != (lower == up)) {
+            v = vo;
+            ix = io;
+          }
+        }
+      }
+      cval[lane] = v;
+      cidx[lane] = ix;
+    }
+    __syncthreads();
+  }
+  for (int size = 2; filled > 64 && size <= kSampleThreads; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const int partner = tid ^ stride;
       if (partner > tid) {
@@ -268,7 +332,27 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   // 4. Weights, then the cumulative sums and the draw in ranking order.
   if (tid < p.k) cum[tid] = expf((cval[tid] - cval[0]) * p.inv_t);
   __syncthreads();
-  if (tid == 0) {
+  if (p.k <= 64) {
+    // One wave: inclusive scan of the weights across lanes, then the cut and
+    // the draw as the first lane (rank) whose sum passes each threshold.
+    if (wave == 0) {
+      float c = lane < p.k ? cum[lane] : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(c, off, 64);
+        if (lane >= off) c += o;
+      }
+      const float total = __shfl(c, p.k - 1, 64);
+      const uint64_t in_k = p.k == 64 ? ~0ull : ((1ull << p.k) - 1ull);
+      const uint64_t over_p = __ballot(c >= p.top_p * total) & in_k;
+      const int cut = over_p ? __builtin_ctzll(over_p) : p.k - 1;
+      const float target = p.u[blockIdx.x] * __shfl(c, cut, 64);
+      const uint64_t upto_cut = cut == 63 ? ~0ull : ((1ull << (cut + 1)) - 1ull);
+      const uint64_t over_u = __ballot(c > target) & upto_cut;
+      const int pick = over_u ? __builtin_ctzll(over_u) : cut;
+      if (lane == 0) p.tokens[blockIdx.x] = cidx[pick];
+    }
+  } else if (tid == 0) {
     float c = 0.f;
     for (int j = 0; j < p.k; ++j) {
       c += cum[j];
