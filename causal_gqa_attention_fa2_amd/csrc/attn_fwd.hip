@@ -218,33 +218,34 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   // Packed keys and values: the tile's first row is a wave-uniform base in
   // SGPRs and each lane adds a 32-bit byte offset fixed for the kernel
   // (recomputed with the clamp only on the sequence's last tile).
+  // Paged keys and values: the RPI rows of one copy instruction lie in one
+  // 16-token block, so the base is that instruction's first row and the
+  // lane's row is lane / CH rows further (clamped like the row itself).
   auto copy_off = [&](int i, int last, bool tr) {
     const int r = (wave * IPW + i) * RPI + lane / CH;
     const int col = tr ? swz_tr<D>(r, (lane % CH) * 8) : swz<D>(r, (lane % CH) * 8);
-    return (uint32_t)(min(r, last) * p.h_kv * D + col) * 2u;
+    const int rr = PAGED ? lane / CH : r;
+    return (uint32_t)(min(rr, last) * p.h_kv * D + col) * 2u;
   };
   uint32_t koffc[IPW], voffc[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    koffc[i] = copy_off(i, kBC - 1, false);
-    voffc[i] = copy_off(i, kBC - 1, true);
+    koffc[i] = copy_off(i, PAGED ? RPI - 1 : kBC - 1, false);
+    voffc[i] = copy_off(i, PAGED ? RPI - 1 : kBC - 1, true);
   }
   const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
   auto issue_tile = [&](int kt, int stage) {
     if constexpr (PAGED) {
+      const bool tail = kt * kBC + kBC > Lk;  // wave-uniform
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const int r = (wave * IPW + i) * RPI + lane / CH;
-        const int slot = (lane % CH) * 8;
         const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
         const int lb = min(t0 >> 4, p.max_blocks - 1);
         const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
-        const int t = min(kt * kBC + r, Lk - 1);
-        const size_t row = ((size_t)(phys * 16 + (t - (lb << 4))) * p.h_kv + g) * D;
-        f16* kdst = Ks[stage] + (wave * IPW + i) * 64 * 8;
-        f16* vdst = Vs[stage] + (wave * IPW + i) * 64 * 8;
-        dma16(p.k + row + swz<D>(r, slot), kdst);
-        dma16(p.v + row + swz_tr<D>(r, slot), vdst);
+        const size_t base = ((size_t)(phys * 16 + (t0 - (lb << 4))) * p.h_kv + g) * D;
+        const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+        dma16s_at(p.k + base, tail ? copy_off(i, Lk - 1 - t0, false) : koffc[i], ks_lds + dst);
+        dma16s_at(p.v + base, tail ? copy_off(i, Lk - 1 - t0, true) : voffc[i], vs_lds + dst);
       }
     } else {
       const int k0 = kt * kBC;
