@@ -739,43 +739,64 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 
 
 // Row terms of the backward for every (token, query head) row: -D =
-// -rowsum(dO * O) and LSE * log2(e), stored [h_q, T]. A group of D/8 lanes owns a row.
+// -rowsum(dO * O) and LSE * log2(e), stored [h_q, T]. A work-group takes
+// tiles of 16 tokens x 16 heads: it reads their O and dO rows in memory
+// order (a group of D/8 lanes per row), gathers D in LDS, and then reads the
+// LSE and writes the two terms token-contiguously for each head.
+constexpr int kRowsTB = 16, kRowsHC = 16;  // tokens and heads per tile
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;  // rows per work-group and pass
-  constexpr int kU = 4;           // rows per group in flight
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int RPP = 256 / LPR;         // rows per pass
+  constexpr int PASSES = kRowsTB * kRowsHC / RPP;
+  constexpr int kU = 4;                  // passes in flight
+  static_assert(PASSES % kU == 0 && kRowsTB * kRowsHC == 256, "tile must split over the passes");
+  __shared__ float dsh[kRowsHC][kRowsTB + 1];
   const int tid = threadIdx.x;
   const int gl = tid % LPR;
-  const int n = p.T * p.h_q;  // < 2^31
-  const int stride = gridDim.x * RPB;
-  for (int row0 = blockIdx.x * RPB + tid / LPR; row0 < n; row0 += kU * stride) {
-    f16x8 ov[kU], gv[kU];
+  const int rg = tid / LPR;
+  const int nhc = (p.h_q + kRowsHC - 1) / kRowsHC;
+  const int n_tiles = (p.T + kRowsTB - 1) / kRowsTB * nhc;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int t0 = tile / nhc * kRowsTB;
+    const int h0 = tile % nhc * kRowsHC;
+#pragma unroll 1
+    for (int ps = 0; ps < PASSES; ps += kU) {
+      f16x8 ov[kU], gv[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int row = row0 + u * stride;  // t * h_q + h
-      if (row < n) {
-        ov[u] = *(const f16x8*)(p.o + (size_t)row * D + 8 * gl);
-        gv[u] = *(const f16x8*)(p.dout + (size_t)row * D + 8 * gl);
+      for (int u = 0; u < kU; ++u) {
+        const int r = (ps + u) * RPP + rg;  // (token, head) of the tile, heads fastest
+        const int t = t0 + r / kRowsHC, h = h0 + r % kRowsHC;
+        if (t < p.T && h < p.h_q) {
+          const size_t row = (size_t)t * p.h_q + h;
+          ov[u] = *(const f16x8*)(p.o + row * D + 8 * gl);
+          gv[u] = *(const f16x8*)(p.dout + row * D + 8 * gl);
+        } else {
+          ov[u] = gv[u] = f16x8{};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)gv[u][e] * (float)ov[u][e];
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+        const int r = (ps + u) * RPP + rg;
+        if (gl == 0) dsh[r % kRowsHC][r / kRowsHC] = acc;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int row = row0 + u * stride;
-      if (row >= n) break;  // uniform over the group
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)gv[u][e] * (float)ov[u][e];
-#pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-      if (gl == 0) {
-        const int t = row / p.h_q;
-        const int h = row - t * p.h_q;
+    __syncthreads();
+    {
+      const int hl = tid / kRowsTB, tl = tid % kRowsTB;
+      const int h = h0 + hl, t = t0 + tl;
+      if (h < p.h_q && t < p.T) {
         const size_t i = (size_t)h * p.T + t;
-        p.drow[i] = -acc;
+        p.drow[i] = -dsh[hl][tl];
         p.lse2[i] = p.lse[i] * kLog2e;
       }
     }
+    __syncthreads();
   }
 }
 
@@ -1015,9 +1036,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
   const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);  // persistent dq grids
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
-  const long long rows = (long long)a.total_tokens * a.h_q;
-  const int rpb = 256 / (a.head_dim / 8);
-  const long long wgs = (rows + rpb - 1) / rpb;
+  const long long wgs = (long long)((a.total_tokens + kRowsTB - 1) / kRowsTB) *
+                        ((a.h_q + kRowsHC - 1) / kRowsHC);  // row-term tiles
   const dim3 gr((unsigned)(wgs < 4 * a.num_cus ? wgs : 4 * a.num_cus));
   const bool ds = a.ds != nullptr;
   if (a.rope_cos != nullptr) {
