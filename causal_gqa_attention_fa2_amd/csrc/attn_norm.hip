@@ -103,7 +103,10 @@ template <int LPR>
 __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams p) {
   constexpr int GPW = kNormBwdThreads / LPR;  // row groups per work-group
   constexpr int PPL = pieces_per_lane<LPR>();
-  __shared__ float red[kNormMaxCols];
+  // One row of dw terms per group: GPW * n floats, at most 16 * 2048 (LPR =
+  // 64 serves n >= 512) or GPW * 16 LPR (below that n < 16 LPR) = 64 KiB.
+  constexpr int kRed = LPR == 64 ? 16 * kNormMaxCols : GPW * 16 * LPR;
+  __shared__ float red[kRed];
   const int lane = threadIdx.x & 63;
   const int gl = lane % LPR;
   const int grp = threadIdx.x / LPR;  // 0 .. GPW - 1
@@ -150,27 +153,26 @@ __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams
       }
     }
   }
-  // Sum the GPW groups' dw terms in group order: group 0 stores, then each
-  // later group adds its terms in turn (one barrier per group).
+  // Sum the GPW groups' dw terms in group order: every group stores its row
+  // of terms in LDS, then each column is added up over the groups in order
+  // (the same sequence of fp32 additions as adding the groups one by one,
+  // with two barriers instead of one per group).
   const int n = p.pieces * 8;
-  for (int s = 0; s < GPW; ++s) {
-    if (grp == s) {
 #pragma unroll
-      for (int k = 0; k < PPL; ++k) {
-        const int c = gl + k * LPR;
-        if (c < p.pieces) {
+  for (int k = 0; k < PPL; ++k) {
+    const int c = gl + k * LPR;
+    if (c < p.pieces) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float* dst = &red[c * 8 + e];
-            *dst = (s == 0 ? 0.f : *dst) + acc[k][e];
-          }
-        }
-      }
+      for (int e = 0; e < 8; ++e) red[grp * n + c * 8 + e] = acc[k][e];
     }
-    __syncthreads();
   }
+  __syncthreads();
   float* prow = p.part + (size_t)blockIdx.x * n;
-  for (int j = threadIdx.x; j < n; j += kNormBwdThreads) prow[j] = red[j];
+  for (int j = threadIdx.x; j < n; j += kNormBwdThreads) {
+    float t = 0.f;
+    for (int g = 0; g < GPW; ++g) t += red[g * n + j];
+    prow[j] = t;
+  }
 }
 
 // dw_j = sum of the partial rows. A work-group owns 64 columns; its four
