@@ -741,16 +741,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 // Row terms of the backward for every (token, query head) row: -D =
 // -rowsum(dO * O) and LSE * log2(e), stored [h_q, T]. A work-group takes
 // tiles of 16 tokens x 16 heads: it reads their O and dO rows in memory
-// order (a group of D/8 lanes per row), gathers D in LDS, and then reads the
-// LSE and writes the two terms token-contiguously for each head.
+// order (a group of D/8 lanes per row, every row of the tile in flight at
+// once; rows past the batch read its last row and are not stored), sums each
+// row with v_dot2 products and DPP lane moves, gathers D in LDS, and then
+// reads the LSE and writes the two terms token-contiguously for each head.
 constexpr int kRowsTB = 16, kRowsHC = 16;  // tokens and heads per tile
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
   constexpr int LPR = D / 8;             // lanes per row
   constexpr int RPP = 256 / LPR;         // rows per pass
   constexpr int PASSES = kRowsTB * kRowsHC / RPP;
-  constexpr int kU = 4;                  // passes in flight
-  static_assert(PASSES % kU == 0 && kRowsTB * kRowsHC == 256, "tile must split over the passes");
+  static_assert(kRowsTB * kRowsHC == 256 && PASSES * RPP == 256, "tile must split over the passes");
   __shared__ float dsh[kRowsHC][kRowsTB + 1];
   const int tid = threadIdx.x;
   const int gl = tid % LPR;
@@ -760,31 +761,25 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdParams p) {
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int t0 = tile / nhc * kRowsTB;
     const int h0 = tile % nhc * kRowsHC;
-#pragma unroll 1
-    for (int ps = 0; ps < PASSES; ps += kU) {
-      f16x8 ov[kU], gv[kU];
+    f16x8 ov[PASSES], gv[PASSES];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int r = (ps + u) * RPP + rg;  // (token, head) of the tile, heads fastest
-        const int t = t0 + r / kRowsHC, h = h0 + r % kRowsHC;
-        if (t < p.T && h < p.h_q) {
-          const size_t row = (size_t)t * p.h_q + h;
-          ov[u] = *(const f16x8*)(p.o + row * D + 8 * gl);
-          gv[u] = *(const f16x8*)(p.dout + row * D + 8 * gl);
-        } else {
-          ov[u] = gv[u] = f16x8{};
-        }
-      }
+    for (int u = 0; u < PASSES; ++u) {
+      const int r = u * RPP + rg;  // (token, head) of the tile, heads fastest
+      const int t = min(t0 + r / kRowsHC, p.T - 1), h = min(h0 + r % kRowsHC, p.h_q - 1);
+      const size_t row = (size_t)t * p.h_q + h;
+      ov[u] = *(const f16x8*)(p.o + row * D + 8 * gl);
+      gv[u] = *(const f16x8*)(p.dout + row * D + 8 * gl);
+    }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        float acc = 0.f;
+    for (int u = 0; u < PASSES; ++u) {
+      float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)gv[u][e] * (float)ov[u][e];
-#pragma unroll
-        for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-        const int r = (ps + u) * RPP + rg;
-        if (gl == 0) dsh[r % kRowsHC][r / kRowsHC] = acc;
-      }
+      for (int e = 0; e < 8; e += 2)
+        acc = __builtin_amdgcn_fdot2(f16x2{gv[u][e], gv[u][e + 1]}, f16x2{ov[u][e], ov[u][e + 1]},
+                                     acc, false);
+      acc = group_sum<LPR>(acc);
+      const int r = u * RPP + rg;
+      if (gl == 0) dsh[r % kRowsHC][r / kRowsHC] = acc;
     }
     __syncthreads();
     {

@@ -90,22 +90,6 @@ __device__ __forceinline__ int ctx_of(const DecParams& p, int b) {
   return min(max(p.ctx[b], 0), p.max_ctx);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over each aligned group of N lanes (N = 8 or 16) with DPP moves; every
-// lane of the group ends with the total.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
-  x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8-lane half
-  if constexpr (N == 16) x += dpp_mov<0x140>(x);  // row_mirror: other half of the row
-  return x;
-}
-
 // Two fp16 values (lo from a, hi from b) taken from the same half of two words.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -63,6 +63,25 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane move by a DPP control (the source lane's value; 0 where the pattern
+// has none).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of N lanes (N = 8 or 16) with DPP moves; every
+// lane of the group ends with the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8-lane half
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);  // row_mirror: other half of the row
+  return x;
+}
+
 // Lane index (0..63) recomputed where it is used (two VALU instructions that
 // the compiler can neither hoist nor keep live), for per-lane constants that
 // are cheaper to rebuild than to hold in registers through a loop.
