@@ -644,7 +644,7 @@ def main():
     parts = {
         "attn_fwd": dict(t=t_fwd, bound="mfma", achieved=f_fwd / t_fwd / 1e12,
                          peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_fwd,
-                         launches=["fwd_kernel<128, false, false>"]),
+                         launches=["fwd_kernel<128, false, false, 8>"]),
         "attn_bwd": dict(t=t_bwd, bound="mfma", achieved=f_bwd / t_bwd / 1e12,
                          peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s", alg=f_bwd,
                          launches=["dq_kernel<128, false>", "dkdv_kernel<128, false, false>"]),

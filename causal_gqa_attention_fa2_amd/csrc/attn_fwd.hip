@@ -9,17 +9,23 @@
 // LSE = m + ln l for the backward pass. FP16 inputs, FP32 accumulation
 // (pitchhut "Key Features", item 1).
 //
-// Work decomposition. One work-group of eight waves per (sequence, query
-// tile, KV head, head chunk): hpw heads of the KV head's group times
-// 32 * 8 / hpw query positions, one wave per (head, 32 positions). For the
-// usual group sizes (1, 2, 4, 8) there is one chunk, so every K/V tile is
-// read from HBM once per KV head and shared by all G heads through LDS
-// (grouped-query sharing); eight waves (two per SIMD) share each tile.
+// Work decomposition. One work-group of W waves per (sequence, query tile,
+// KV head, head chunk): hpw heads of the KV head's group times 32 * W / hpw
+// query positions, one wave per (head, 32 positions). For the usual group
+// sizes (1, 2, 4, 8) there is one chunk, so every K/V tile is read from HBM
+// once per work-group and shared by its G heads through LDS (grouped-query
+// sharing).
 //
-// K/V tiles of 64 keys pass through a three-stage LDS ring filled by direct
-// global-to-LDS copies (no staging registers): the copies of tile t+2 are
-// issued right after the barrier that opens tile t, so they have the compute
-// of tiles t and t+1 to arrive; one barrier per tile. K is stored with the
+// Two shapes, chosen from the batch's dims (launch_fwd_impl):
+//   W = 8 (long sequences): eight waves, two per SIMD, share each K/V tile;
+//     a three-stage LDS ring (96 KB at d = 128) whose copies of tile t+2 are
+//     issued right after the barrier that opens tile t, so they have the
+//     compute of tiles t and t+1 to arrive. One work-group per CU.
+//   W = 4 (sequences up to 4096): four waves and a two-stage ring (64 KB),
+//     copies of tile t+1 issued at tile t, so two independent work-groups
+//     share each CU: one's prologue, epilogue and barrier waits overlap the
+//     other's tiles, and the two waves of a SIMD are not tied to one barrier.
+// Either way one barrier per tile. K is stored with the
 // row-read chunk swizzle and V with the transpose-read swizzle (cdna4.h), so
 // both operand loads are free of bank conflicts.
 //
@@ -47,8 +53,7 @@ namespace {
 
 constexpr int kBC = 64;                // keys per tile
 constexpr float kLazy = 8.f;           // headroom (log2 units) of the softmax reference
-constexpr int kStages = 3;             // LDS ring depth
-constexpr int kNTH = 64 * kQWaves;     // threads per work-group
+constexpr int kStages = 3;             // LDS ring depth with eight waves (two with four)
 
 struct FwdParams {
   const f16* __restrict__ q;
@@ -143,19 +148,21 @@ __device__ __forceinline__ bool varlen_item(const FwdParams& p, int k, int lane,
 // and values of position t are slot t % 16 of pool block bt[b][t / 16].
 // ROPE (paged only): the queries are rotated by their context positions as
 // they are loaded (the keys were rotated when they were appended).
-template <int D, bool PAGED, bool ROPE = false>
-__global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
+template <int D, bool PAGED, bool ROPE, int W>
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p) {
+  static_assert(W == 8 || W == 4, "eight or four waves");
+  constexpr int NS = W == 8 ? kStages : 2;  // ring stages
   static_assert(PAGED || !ROPE, "query rotation is a prefill option");
   constexpr int NT = D / 16;   // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;   // 32-wide output blocks over the head dimension
   constexpr int CH = D / 8;    // 16-byte chunks per row
   constexpr int RPI = 64 / CH; // tile rows per copy instruction
-  constexpr int IPW = kBC * CH / 64 / kQWaves;  // copy instructions per wave per tensor
-  static_assert(IPW >= 1 && kBC * CH == 64 * kQWaves * IPW, "tile must split over the waves");
+  constexpr int IPW = kBC * CH / 64 / W;  // copy instructions per wave per tensor
+  static_assert(IPW >= 1 && kBC * CH == 64 * W * IPW, "tile must split over the waves");
   // K (row reads, chunk swizzle) and V (transpose reads, transpose swizzle)
   // tiles, unpadded so that the direct copies fill them in lane order.
-  __shared__ __attribute__((aligned(16))) f16 Ks[kStages][kBC * D];
-  __shared__ __attribute__((aligned(16))) f16 Vs[kStages][kBC * D];
+  __shared__ __attribute__((aligned(16))) f16 Ks[NS][kBC * D];
+  __shared__ __attribute__((aligned(16))) f16 Vs[NS][kBC * D];
 
   const int BR = 32 * p.nqb;
   // Heaviest query tiles (the last ones of the longest sequences) first.
@@ -302,15 +309,23 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
     voff[db] = r * D + swz_tr<D>(r, 32 * db + 16 * (grp & 1) + 4 * (j16 & 3));
   }
 
-  // One tile step on ring stage S = kt % 3 (a compile-time constant); the
-  // copies of tile kt + 2 go to stage (S + 2) % 3, which held tile kt - 1.
+  // One tile step on ring stage S = kt % NS (a compile-time constant).
+  // Three stages: the copies of tile kt + 2 go to stage (S + 2) % 3, which
+  // held tile kt - 1. Two stages: those of tile kt + 1 go to stage
+  // (S + 1) % 2, which held tile kt - 1.
   auto step = [&](int kt, auto S) {
     constexpr int stage = decltype(S)::value;
-    // Tile kt has landed (this wave's copies; tile kt + 1's may still fly),
-    // then every wave's copies have, and every wave is done with tile kt - 1.
-    if (kt + 1 < n_kt) wait_vm_barrier<2 * IPW>();
-    else wait_vm_barrier<0>();
-    if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % kStages);
+    // Tile kt has landed (this wave's copies; with three stages tile
+    // kt + 1's may still fly), then every wave's copies have, and every wave
+    // is done with tile kt - 1.
+    if constexpr (NS == 3) {
+      if (kt + 1 < n_kt) wait_vm_barrier<2 * IPW>();
+      else wait_vm_barrier<0>();
+      if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % NS);
+    } else {
+      wait_vm_barrier<0>();
+      if (kt + 1 < n_kt) issue_tile(kt + 1, (stage + 1) % NS);
+    }
 
     if (!wave_has_rows || kt * kBC > q0a + 31) return;  // fully masked for this wave
     const f16* Kb = Ks[stage];
@@ -415,11 +430,13 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
   // (whose effect the compiler tracks), so it places no wait of its own inside
   // the loop, where such a wait would also stall on the copies in flight.
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0); tile 0 included
-  if (n_kt > 1) issue_tile(1, 1);
-  for (int kt = 0; kt < n_kt; kt += kStages) {
+  if (NS == 3 && n_kt > 1) issue_tile(1, 1);
+  for (int kt = 0; kt < n_kt; kt += NS) {
     step(kt, std::integral_constant<int, 0>{});
     if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
-    if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
+    if constexpr (NS == 3) {
+      if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   const float l_tot = half_swap_sum(l_run);  // all lanes take part in the exchange
@@ -444,6 +461,21 @@ __global__ __launch_bounds__(kNTH, 1) void fwd_kernel(FwdParams p) {
 
 namespace {
 
+template <bool PAGED, int W>
+void launch_fwd_shape(const FwdParams& p, const FwdArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(64 * W);
+  if (PAGED && a.rope_cos != nullptr) {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((fwd_kernel<128, true, true, W>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_kernel<64, true, true, W>), grid, block, 0, stream, p);
+  } else if (a.head_dim == 128) {
+    hipLaunchKernelGGL((fwd_kernel<128, PAGED, false, W>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<64, PAGED, false, W>), grid, block, 0, stream, p);
+  }
+}
+
 template <bool PAGED>
 hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   FwdParams p;
@@ -466,7 +498,13 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   p.h_q = a.h_q;
   p.h_kv = a.h_kv;
   p.G = a.h_q / a.h_kv;
-  const QTileLayout lay = qtile_layout(p.G);
+  // Sequences (or contexts) up to 4096 keys take four-wave work-groups, two
+  // per CU; longer ones eight-wave work-groups, one per CU (same-run timing:
+  // the four-wave shape is 2-8% faster up to 4096 keys and 1-3% slower at
+  // 8192).
+  const int max_keys = PAGED ? a.max_ctx_len : a.max_seqlen;
+  const int W = max_keys <= 4096 ? 4 : 8;
+  const QTileLayout lay = qtile_layout(p.G, W);
   p.hpw = lay.hpw;
   p.nqb = lay.nqb;
   p.n_chunks = lay.n_chunks;
@@ -481,16 +519,10 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   p.mapped = items < slots && a.n_seqs <= kMapSeqs &&
              (long long)a.n_seqs * ((p.n_qtiles + 63) / 64) <= 512;
   const dim3 grid((unsigned)((p.mapped ? items : slots) * a.h_kv * p.n_chunks));
-  if (PAGED && a.rope_cos != nullptr) {
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL((fwd_kernel<128, true, true>), grid, dim3(kNTH), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<64, true, true>), grid, dim3(kNTH), 0, stream, p);
-  } else if (a.head_dim == 128) {
-    hipLaunchKernelGGL((fwd_kernel<128, PAGED>), grid, dim3(kNTH), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((fwd_kernel<64, PAGED>), grid, dim3(kNTH), 0, stream, p);
-  }
+  if (W == 4)
+    launch_fwd_shape<PAGED, 4>(p, a, grid, stream);
+  else
+    launch_fwd_shape<PAGED, 8>(p, a, grid, stream);
   return hipGetLastError();
 }
 

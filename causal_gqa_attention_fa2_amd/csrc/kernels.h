@@ -132,19 +132,19 @@ inline int decode_num_wgs(int n_seqs, int max_ctx_len) {
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 hipError_t decode_scratch(void** ptr);
 
-// Query-stationary work-groups (forward and dQ) have kQWaves waves; each wave
-// owns 32 query rows of one head. A work-group covers hpw heads of a KV
-// group (hpw = the largest power of two <= min(G, kQWaves)) and
-// 32 * kQWaves / hpw query positions; a group of G heads needs
-// ceil(G / hpw) head chunks.
+// Query-stationary work-groups have `waves` waves (dQ: kQWaves; the forward:
+// kQWaves or 4, by sequence length); each wave owns 32 query rows of one
+// head. A work-group covers hpw heads of a KV group (hpw = the largest power
+// of two <= min(G, waves)) and 32 * waves / hpw query positions; a group of
+// G heads needs ceil(G / hpw) head chunks.
 constexpr int kQWaves = 8;
 struct QTileLayout {
   int hpw, nqb, n_chunks;
 };
-inline QTileLayout qtile_layout(int G) {
+inline QTileLayout qtile_layout(int G, int waves = kQWaves) {
   int hpw = 1;
-  while (hpw * 2 <= G && hpw * 2 <= kQWaves) hpw *= 2;
-  return QTileLayout{hpw, kQWaves / hpw, (G + hpw - 1) / hpw};
+  while (hpw * 2 <= G && hpw * 2 <= waves) hpw *= 2;
+  return QTileLayout{hpw, waves / hpw, (G + hpw - 1) / hpw};
 }
 
 // RMSNorm over rows of n fp16 values (n % 8 == 0, 8 <= n <= kNormMaxCols).
