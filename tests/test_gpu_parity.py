@@ -70,6 +70,24 @@ def test_random_shapes(gpu, lens, h_q, h_kv, d, seed):
     check_bwd(name, inp, dq, dk, dv)
 
 
+@pytest.mark.parametrize("h_q,h_kv,d", [(2, 2, 128), (6, 2, 64), (16, 1, 64), (8, 1, 128)],
+                         ids=lambda x: str(x))
+def test_long_batch_group_sizes(gpu, h_q, h_kv, d):
+    """A batch longer than 4096 keys takes the eight-wave forward (shorter
+    ones the four-wave shape, covered above): group sizes 1, 3, 16 and 8 and
+    both head dims, a sequence just past the threshold plus a short one and
+    an edge length, compared in full with the oracle."""
+    lens = [4100, 65, 300]
+    name = f"long hq{h_q} hkv{h_kv} d{d}"
+    inp = W.make_train_inputs(lens, h_q, h_kv, d, seed=2300 + h_q + 7 * h_kv + d)
+    dd = dev(inp, gpu)
+    o, lse = gpu_fwd(dd)
+    dq, dk, dv = gpu_bwd(dd, o, lse)
+    torch.cuda.synchronize()
+    check_fwd(name, inp, o, lse)
+    check_bwd(name, inp, dq, dk, dv)
+
+
 def test_tiny_workload(gpu):
     inp = W.workload_inputs("tiny")
     dd = dev(inp, gpu)
