@@ -239,10 +239,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   // The tile's first row is a wave-uniform base in SGPRs; each lane adds a
   // 32-bit byte offset fixed for the kernel, recomputed with the clamp only
   // on the sequence's last tile.
+  // With RoPE (whose epilogue needs registers) the lane id is rebuilt at each
+  // issue, so the compiler cannot keep the offsets live through the loop;
+  // without, the offsets stay in registers (cheaper per tile).
   const int tsel = (wave * CPW) / NI;  // K (waves 0-3) or V (4-7)
   auto copy_off = [&](int c, int last) {
-    const int r = ((wave * CPW) % NI + c) * RPI + lane / CH;
-    return (uint32_t)(min(r, last) * p.h_kv * D + swz<D>(r, (lane % CH) * 8)) * 2u;
+    const int ln = ROPE ? lane_id_fresh() : lane;
+    const int r = ((wave * CPW) % NI + c) * RPI + ln / CH;
+    return (uint32_t)(min(r, last) * p.h_kv * D + swz<D>(r, (ln % CH) * 8)) * 2u;
   };
   const uint32_t smem_lds = lds_addr(smem);
   auto issue_tile = [&](const Item& it, int kt, int st) {
