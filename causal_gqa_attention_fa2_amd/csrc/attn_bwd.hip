@@ -561,17 +561,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 
   // Team 1's dS block of query block m (32 rows x the pair's 32 keys) to the
   // workspace for the dQ kernel, lane-major: lane l's 16 values (rows
-  // 8(i/4) + 4hi + i%4 of key column l % 32) at halves 16 l .. 16 l + 15.
-  // Pairs wholly past the sequence store nothing. The stores count in vmcnt,
-  // so the next iteration's copy wait also waits for them.
+  // 8(i/4) + 4hi + i%4 of key column l % 32) at halves 16 l .. 16 l + 15,
+  // with the two 8-value halves swapped for lanes 32..63 (so that the dQ
+  // kernel's transpose reads of lanes l and l + 32, 1 KiB apart, fall in
+  // different LDS banks). Pairs wholly past the sequence store nothing. The
+  // stores count in vmcnt, so the next iteration's copy wait also waits for
+  // them.
   auto store_ds = [&](int m, const f16x8* f) {
     if (kw0 >= L) return;
     const int head = g * p.G + m / n_qb;
     const int qb = qb_begin + m % n_qb;
     f16* dst = p.ds + ((((size_t)b * p.h_q + head) * p.nbmax + qb) * p.nbmax + (kw0 >> 5)) * 1024 +
                lane * 16;
-    *(f16x8*)dst = f[0];
-    *(f16x8*)(dst + 8) = f[1];
+    *(f16x8*)(dst + 8 * hi) = f[0];
+    *(f16x8*)(dst + 8 - 8 * hi) = f[1];
   };
 
   // Iteration j of team TEAM on the ring stage of its block (a compile-time
@@ -903,7 +906,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
   // Per-lane LDS offsets (halves). K^T: rows 8hi + 4r + j16/4 (+ 16u),
   // columns 32db + 16(grp&1) + 4(j16&3). dS^T: lane 4e + jj of group grp
   // reads the chunk of stored lane 32 (jj&1) + 16u + 8(grp>>1) + 4r + e,
-  // chunk 2(grp&1) + jj/2.
+  // chunk 2(grp&1) + jj/2, which for stored lanes 32..63 sits at chunk
+  // position c ^ 2 (the dK/dV kernel swaps their halves).
   int kto[2][ND];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -921,7 +925,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
         dso[u][r] = (32 * (jj & 1) + 16 * u + 8 * (grp >> 1) + 4 * r + e) * 16 +
-                    4 * (2 * (grp & 1) + (jj >> 1));
+                    4 * ((2 * (grp & 1) + (jj >> 1)) ^ (2 * (jj & 1)));
     }
   }
 
