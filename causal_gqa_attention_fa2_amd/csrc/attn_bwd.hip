@@ -481,6 +481,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   const int qb_begin = k_wg0 / 32;
   const int n_qb = (L + 31) / 32 - qb_begin;
   const int n_it = p.G * n_qb;
+  // Block m is query block qb_begin + m % n_qb of head m / n_qb of the group.
+  // Blocks are issued and processed in order, so each stream keeps its
+  // (head, block) pair as counters instead of dividing by n_qb per block (a
+  // runtime division costs some 25 scalar instructions).
+  struct BlkPos {
+    int h, qb;
+  };
+  auto advance = [&](BlkPos& ps) {
+    if (++ps.qb == n_qb) {
+      ps.qb = 0;
+      ++ps.h;
+    }
+  };
 
   // Copies of block m into stage st: team-0 wave w4 issues CPW of the block's
   // 2 * IPB copy instructions, all of one tensor (Q for w4 < 2, dO after);
@@ -500,10 +513,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int c = 0; c < CPW; ++c) coff[c] = copy_off(c, 31);
   const uint32_t xs_lds = lds_addr(&Xs[0][0][0]);
-  auto issue_blk = [&](int m, auto ST) {
+  BlkPos ipos{0, 0};  // next block to issue (team 0)
+  auto issue_blk = [&](auto ST) {
     constexpr int st = decltype(ST)::value;
-    const int head = g * p.G + m / n_qb;
-    const int q0 = (qb_begin + m % n_qb) * 32;
+    const int head = g * p.G + ipos.h;
+    const int q0 = (qb_begin + ipos.qb) * 32;
+    advance(ipos);
     const f16* base = (tsel ? p.dout : p.q) + ((size_t)(s0 + q0) * p.h_q + head) * D;
     const bool tail = q0 + 31 >= L;  // wave-uniform
 #pragma unroll
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 
   // Block 0's copies go out before the ordinary loads below, so the two
   // latencies overlap.
-  if (team == 0) issue_blk(0, std::integral_constant<int, 0>{});
+  if (team == 0) issue_blk(std::integral_constant<int, 0>{});
 
   // K (team 0) or V (team 1) of the pair's keys as the B operand: lane holds
   // row `key` (rows past the end read the last row; never stored), columns
@@ -567,16 +582,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   // different LDS banks). Pairs wholly past the sequence store nothing. The
   // stores count in vmcnt, so the next iteration's copy wait also waits for
   // them.
-  auto store_ds = [&](int m, const f16x8* f) {
+  auto store_ds = [&](const BlkPos& ps, const f16x8* f) {
     if (kw0 >= L) return;
-    const int head = g * p.G + m / n_qb;
-    const int qb = qb_begin + m % n_qb;
+    const int head = g * p.G + ps.h;
+    const int qb = qb_begin + ps.qb;
     f16* dst = p.ds + ((((size_t)b * p.h_q + head) * p.nbmax + qb) * p.nbmax + (kw0 >> 5)) * 1024 +
                lane * 16;
     *(f16x8*)(dst + 8 * hi) = f[0];
     *(f16x8*)(dst + 8 - 8 * hi) = f[1];
   };
 
+  BlkPos cpos{0, 0};  // next block to process
   // Iteration j of team TEAM on the ring stage of its block (a compile-time
   // constant: the loop below is unrolled by the ring depth, and j = J mod 4).
   // Team 0 works on block j, team 1 on block j - 1.
@@ -596,14 +612,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
       }
       // Stage (j + 2) % 4 last held block j - 2, which team 1 finished in
       // the previous iteration.
-      if (j + 2 < n_it)
-        issue_blk(j + 2, std::integral_constant<int, (decltype(J)::value + 2) % kKvStages>{});
+      if (j + 2 < n_it) issue_blk(std::integral_constant<int, (decltype(J)::value + 2) % kKvStages>{});
     }
     const int m = j - tm;
     if (m < 0 || m >= n_it) return;  // uniform over the wave
     constexpr int st = (decltype(J)::value - tm + kKvStages) % kKvStages;
     constexpr int par = (decltype(J)::value - tm + kKvStages) & 1;  // m & 1
-    const int q0 = (qb_begin + m % n_qb) * 32;
+    const BlkPos mpos = cpos;  // block m
+    advance(cpos);
+    const int q0 = (qb_begin + mpos.qb) * 32;
     const f16* Xb = &Xs[st][0][0];
 
     // Operand reads are issued in blocks ahead of their uses (scheduling
@@ -700,7 +717,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
         }
         f[u] = __builtin_bit_cast(f16x8, w);
       }
-      if constexpr (STORE_DS) store_ds(m, f);
+      if constexpr (STORE_DS) store_ds(mpos, f);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -720,7 +737,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   using I3 = std::integral_constant<int, 3>;
   static_assert(kKvStages == 4, "the loop is unrolled by the ring depth");
   if (team == 0) {
-    if (n_it > 1) issue_blk(1, I1{});
+    if (n_it > 1) issue_blk(I1{});
     for (int j = 0; j <= n_it; j += 4) {
       body(j, I0{}, I0{});
       if (j + 1 <= n_it) body(j + 1, I1{}, I0{});
