@@ -520,13 +520,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     const int q0 = (qb_begin + ipos.qb) * 32;
     advance(ipos);
     const f16* base = (tsel ? p.dout : p.q) + ((size_t)(s0 + q0) * p.h_q + head) * D;
-    const bool tail = q0 + 31 >= L;  // wave-uniform
+    // One branch per block (not per copy) between the fixed offsets and, on
+    // the sequence's last block, the clamped ones.
+    auto copies = [&](bool tail) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int ii = (w4 * CPW) % IPB + c;
-      dma16s_at(base, tail ? copy_off(c, L - 1 - q0) : coff[c],
-                xs_lds + (uint32_t)((st * 2 + tsel) * BLK + ii * 512) * 2u);
-    }
+      for (int c = 0; c < CPW; ++c) {
+        const int ii = (w4 * CPW) % IPB + c;
+        dma16s_at(base, tail ? copy_off(c, L - 1 - q0) : coff[c],
+                  xs_lds + (uint32_t)((st * 2 + tsel) * BLK + ii * 512) * 2u);
+      }
+    };
+    if (q0 + 31 >= L) copies(true);  // wave-uniform
+    else copies(false);
     if (wave == 0) {
       const float* src = (lane < 32 ? p.lse2 : p.drow) + (size_t)head * p.T + s0 +
                          min(q0 + l32, L - 1);

@@ -242,28 +242,36 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
   }
   const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
   auto issue_tile = [&](int kt, int stage) {
+    // One branch per tile (not per copy) between the fixed offsets and, on
+    // the sequence's last tile, the clamped ones.
     if constexpr (PAGED) {
-      const bool tail = kt * kBC + kBC > Lk;  // wave-uniform
+      auto copies = [&](bool tail) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
-        const int lb = min(t0 >> 4, p.max_blocks - 1);
-        const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
-        const size_t base = ((size_t)(phys * 16 + (t0 - (lb << 4))) * p.h_kv + g) * D;
-        const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
-        dma16s_at(p.k + base, tail ? copy_off(i, Lk - 1 - t0, false) : koffc[i], ks_lds + dst);
-        dma16s_at(p.v + base, tail ? copy_off(i, Lk - 1 - t0, true) : voffc[i], vs_lds + dst);
-      }
+        for (int i = 0; i < IPW; ++i) {
+          const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
+          const int lb = min(t0 >> 4, p.max_blocks - 1);
+          const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
+          const size_t base = ((size_t)(phys * 16 + (t0 - (lb << 4))) * p.h_kv + g) * D;
+          const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+          dma16s_at(p.k + base, tail ? copy_off(i, Lk - 1 - t0, false) : koffc[i], ks_lds + dst);
+          dma16s_at(p.v + base, tail ? copy_off(i, Lk - 1 - t0, true) : voffc[i], vs_lds + dst);
+        }
+      };
+      if (kt * kBC + kBC > Lk) copies(true);  // wave-uniform
+      else copies(false);
     } else {
       const int k0 = kt * kBC;
       const size_t base = ((size_t)(s0 + k0) * p.h_kv + g) * D;
-      const bool tail = k0 + kBC > L;  // wave-uniform
+      auto copies = [&](bool tail) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
-        dma16s_at(p.k + base, tail ? copy_off(i, L - 1 - k0, false) : koffc[i], ks_lds + dst);
-        dma16s_at(p.v + base, tail ? copy_off(i, L - 1 - k0, true) : voffc[i], vs_lds + dst);
-      }
+        for (int i = 0; i < IPW; ++i) {
+          const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+          dma16s_at(p.k + base, tail ? copy_off(i, L - 1 - k0, false) : koffc[i], ks_lds + dst);
+          dma16s_at(p.v + base, tail ? copy_off(i, L - 1 - k0, true) : voffc[i], vs_lds + dst);
+        }
+      };
+      if (k0 + kBC > L) copies(true);  // wave-uniform
+      else copies(false);
     }
   };
 
