@@ -157,6 +157,23 @@ def _random_prefill_cases(n, seed):
     return cases
 
 
+@pytest.mark.parametrize("h_q,h_kv,d", [(16, 8, 128), (8, 2, 64)], ids=lambda x: str(x))
+def test_prefill_long_context(gpu, h_q, h_kv, d):
+    """Contexts past 4096 keys take the eight-wave prefill (the cases above,
+    all shorter, take the four-wave shape): a cache of 4200 and one ending
+    just past the threshold, next to short and empty caches."""
+    prior, new = [4200, 4090, 0, 300], [33, 10, 17, 129]
+    inp = W.poison_unused_prefill(W.make_prefill_inputs(prior, new, h_q, h_kv, d,
+                                                        seed=5600 + h_q + d, spare_blocks=2))
+    name = f"prefill long hq{h_q} hkv{h_kv} d{d}"
+    print(name, flush=True)
+    dd, o, lse = _gpu(inp, gpu)
+    ref, kp, vp = _oracle(inp)
+    assert _same_bits(dd["k_pool"], torch.from_numpy(kp))
+    assert _same_bits(dd["v_pool"], torch.from_numpy(vp))
+    _check(name, inp, o, lse, ref)
+
+
 @pytest.mark.parametrize("prior,new,h_q,h_kv,d,seed", _random_prefill_cases(8, 91),
                          ids=lambda x: str(x))
 def test_prefill_random_batches(gpu, prior, new, h_q, h_kv, d, seed):

@@ -104,9 +104,20 @@ def test_append_and_prefill_with_rope(gpu, h_q, h_kv, d):
     slots untouched); attn_prefill_paged_rope equals attn_rope on q followed
     by attn_prefill_paged bit for bit, and the oracle's prefill on the
     rotated tensors within the attention bars."""
-    inp = W.poison_unused_prefill(W.make_prefill_inputs(PRIOR, NEW, h_q, h_kv, d,
-                                                        seed=6200 + h_q + d, spare_blocks=2))
-    name = f"prefill rope hq{h_q} hkv{h_kv} d{d}"
+    _prefill_with_rope(gpu, PRIOR, NEW, h_q, h_kv, d, 6200 + h_q + d,
+                       f"prefill rope hq{h_q} hkv{h_kv} d{d}")
+
+
+@pytest.mark.parametrize("h_q,h_kv,d", [(16, 8, 128), (8, 2, 64)], ids=lambda x: str(x))
+def test_append_and_prefill_with_rope_long_context(gpu, h_q, h_kv, d):
+    """The same checks with contexts past 4096 keys (the eight-wave prefill)."""
+    _prefill_with_rope(gpu, [4200, 4090, 0, 300], [33, 10, 17, 129], h_q, h_kv, d,
+                       6250 + h_q + d, f"prefill rope long hq{h_q} hkv{h_kv} d{d}")
+
+
+def _prefill_with_rope(gpu, prior, new, h_q, h_kv, d, seed, name):
+    inp = W.poison_unused_prefill(W.make_prefill_inputs(prior, new, h_q, h_kv, d,
+                                                        seed=seed, spare_blocks=2))
     print(name, flush=True)
     pos = chunk_positions(inp["cu_q"].numpy(), inp["ctx_lens"].numpy())
     (c, s), tab = _tables(inp["max_ctx"], d, gpu)
