@@ -664,7 +664,7 @@ def main():
 
     configs = {"long_context": train_entry(tr, ts_fwd, ts_bwd)}
     configs["long_context"]["source"] = "the timed steps"
-    for name in ("tiny", "qwen3_train", "grpo_varlen"):
+    for name in ("tiny", "qwen3_train", "grpo_varlen", "long_context_tp8"):
         c = TrainCase(attn, W, name, dev)
         tf, tb = time_launches([c.fwd, c.bwd], max(args.steps, 20), reps=CONFIG_REPS)
         configs[name] = train_entry(c, tf, tb, with_rates=name != "tiny")
@@ -673,7 +673,8 @@ def main():
         len(ts_dec) // 2] / 1e9, 1), "hbm_peak_frac": round(b_dec / sorted(ts_dec)[
             len(ts_dec) // 2] / 1e9 / HBM_PEAK_GBPS, 4), "alg_bytes": int(b_dec),
         "source": "the timed steps"}
-    order = ["tiny", "qwen3_train", "grpo_varlen", "long_context", DECODE_WORKLOAD]
+    order = ["tiny", "qwen3_train", "grpo_varlen", "long_context", "long_context_tp8",
+             DECODE_WORKLOAD]
     configs = {k: configs[k] for k in order}
 
     out = {

@@ -18,6 +18,8 @@ Workloads (shapes of the RL.cu stack's Qwen3-0.6B attention; pitchhut
 * ``grpo_varlen``   4 prompts x 8 samples, prompt U{64..256} shared by a
   prompt's samples, completion U{128..1024} per sample, packed prompt-major
 * ``long_context``  B=4, S=8192, H_q=16, H_kv=8, d=128
+* ``long_context_tp8`` the same batch at one GPU's share of an 8-way split by
+  KV head: H_q=2, H_kv=1, d=128
 * ``paged_decode``  256 sequences, ctx U{128..4096}, block 16, H_q=16,
   H_kv=8, d=128; the logical blocks of all sequences (in order) receive a
   seeded random permutation of the physical blocks.
@@ -39,6 +41,9 @@ TRAIN_WORKLOADS = {
     "qwen3_train": dict(seqlens=[1024] * 8, h_q=16, h_kv=8, d=128, seed=1001),
     "grpo_varlen": dict(seqlens=None, h_q=16, h_kv=8, d=128, seed=1002),
     "long_context": dict(seqlens=[8192] * 4, h_q=16, h_kv=8, d=128, seed=1003),
+    # One GPU's share of long_context split 8 ways by KV head (tensor
+    # parallel): one KV head and its two query heads.
+    "long_context_tp8": dict(seqlens=[8192] * 4, h_q=2, h_kv=1, d=128, seed=1007),
 }
 DECODE_WORKLOADS = {
     "paged_decode": dict(n=256, ctx_lo=128, ctx_hi=4096, block_size=16,

@@ -138,6 +138,7 @@ def test_isolated_bwd_from_oracle_forward(gpu):
     ("qwen3_train", [0, 7], [0, 5]),
     ("grpo_varlen", None, [3]),
     ("long_context", [2], [6]),
+    ("long_context_tp8", [1], [0]),
 ])
 def test_workload_sampled(gpu, workload, seqs, groups):
     """Full-size workload on the GPU (the benchmark's launch), compared with the
