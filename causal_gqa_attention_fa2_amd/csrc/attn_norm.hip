@@ -96,13 +96,14 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_fwd_kernel(NormParams p)
 // Backward, one pass over the rows with 1024-thread work-groups (GPW row
 // groups, four waves per SIMD): dx per row, and this work-group's share of
 // dw. Row group grp of work-group g takes rows g GPW + grp + i n_wgs GPW
-// (grid stride); every lane keeps fp32 dw sums for its pieces, then the
-// work-group adds its groups' sums through LDS in group order and writes one
-// partial row.
-template <int LPR>
+// (grid stride); for rows of 512 to 1024 values, the loads of a group's next
+// row go out before the current row's arithmetic, so two rows' latencies
+// overlap. Every lane keeps fp32 dw
+// sums for its pieces, then the work-group adds its groups' sums through LDS
+// in group order and writes one partial row.
+template <int LPR, int PPL>
 __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams p) {
   constexpr int GPW = kNormBwdThreads / LPR;  // row groups per work-group
-  constexpr int PPL = pieces_per_lane<LPR>();
   // One row of dw terms per group: GPW * n floats, at most 16 * 2048 (LPR =
   // 64 serves n >= 512) or GPW * 16 LPR (below that n < 16 LPR) = 64 KiB.
   constexpr int kRed = LPR == 64 ? 16 * kNormMaxCols : GPW * 16 * LPR;
@@ -117,19 +118,14 @@ __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
   }
   const int stride = gridDim.x * GPW;
-  for (int row = blockIdx.x * GPW + grp; row < p.rows; row += stride) {
-    const h16x8* xr = p.x + (size_t)row * p.pieces;
-    const h16x8* gr = p.dy + (size_t)row * p.pieces;
-    const float r = p.rstd_in[row];
-    h16x8 xv[PPL], gv[PPL], wv[PPL];
+  // dx of one row from its x, dy, w pieces and r; adds the row's dw terms.
+  auto row_grads = [&](int row, const h16x8(&xv)[PPL], const h16x8(&gv)[PPL],
+                       const h16x8(&wv)[PPL], float r) __attribute__((always_inline)) {
     float dot = 0.f;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
       const int c = gl + k * LPR;
       if (c < p.pieces) {
-        xv[k] = xr[c];
-        gv[k] = gr[c];
-        wv[k] = p.w[c];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           dot += (float)gv[k][e] * (float)wv[k][e] * ((float)xv[k][e] * r);
@@ -150,6 +146,87 @@ __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams
           acc[k][e] += g * xh;
         }
         dxr[c] = o;
+      }
+    }
+  };
+  auto load_row = [&](int row, h16x8(&xs)[PPL], h16x8(&gs)[PPL], float& rs)
+                      __attribute__((always_inline)) {
+    const h16x8* xr = p.x + (size_t)row * p.pieces;
+    const h16x8* gr = p.dy + (size_t)row * p.pieces;
+    rs = p.rstd_in[row];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int c = gl + k * LPR;
+      if (c < p.pieces) {
+        xs[k] = xr[c];
+        gs[k] = gr[c];
+      }
+    }
+  };
+  int row = blockIdx.x * GPW + grp;
+  if constexpr (LPR == 64 && PPL == 2) {
+    // Rows of 512 to 1024 values: w stays in registers, and the loads of a
+    // group's next row go out before the current row's arithmetic.
+    h16x8 wv[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int c = gl + k * LPR;
+      if (c < p.pieces) wv[k] = p.w[c];
+    }
+    h16x8 xv[PPL], gv[PPL];
+    float r = 0.f;
+    if (row < p.rows) load_row(row, xv, gv, r);
+    for (; row < p.rows; row += stride) {
+      h16x8 xn[PPL], gn[PPL];
+      float rn = 0.f;
+      if (row + stride < p.rows) load_row(row + stride, xn, gn, rn);
+      row_grads(row, xv, gv, wv, r);
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        xv[k] = xn[k];
+        gv[k] = gn[k];
+      }
+      r = rn;
+    }
+  } else {
+    // Rows are loaded in turn, with the arithmetic written out here (through
+    // row_grads it spills at four pieces per lane). Four pieces per lane
+    // (n > 1024) leave no registers for a second row; for narrow rows (LPR <
+    // 64, several rows per wave) loading ahead measured slower.
+    for (; row < p.rows; row += stride) {
+      const h16x8* xr = p.x + (size_t)row * p.pieces;
+      const h16x8* gr = p.dy + (size_t)row * p.pieces;
+      const float r = p.rstd_in[row];
+      h16x8 xv[PPL], gv[PPL], wv[PPL];
+      float dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        const int c = gl + k * LPR;
+        if (c < p.pieces) {
+          xv[k] = xr[c];
+          gv[k] = gr[c];
+          wv[k] = p.w[c];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            dot += (float)gv[k][e] * (float)wv[k][e] * ((float)xv[k][e] * r);
+        }
+      }
+      const float proj = group_sum<LPR>(dot) * p.inv_n;
+      h16x8* dxr = p.y + (size_t)row * p.pieces;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        const int c = gl + k * LPR;
+        if (c < p.pieces) {
+          h16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xh = (float)xv[k][e] * r;
+            const float g = (float)gv[k][e];
+            o[e] = (h16)(r * (g * (float)wv[k][e] - xh * proj));
+            acc[k][e] += g * xh;
+          }
+          dxr[c] = o;
+        }
       }
     }
   }
@@ -175,27 +252,29 @@ __global__ __launch_bounds__(kNormBwdThreads) void rmsnorm_bwd_kernel(NormParams
   }
 }
 
-// dw_j = sum of the partial rows. A work-group owns 64 columns; its four
-// waves sum the partial rows g = wave, wave + 4, ... (independent loads, so
-// many are in flight), then wave 0 adds the four wave sums in wave order, so
-// the result does not depend on timing.
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_dw_kernel(const float* __restrict__ part,
-                                                                  float* __restrict__ dw,
-                                                                  int n, int n_rows) {
-  __shared__ float sums[kNormThreads];
+// dw_j = sum of the partial rows. A work-group owns 64 columns; its 16
+// waves sum the partial rows g = wave, wave + 16, ... (independent loads, all
+// in flight at once for up to 256 rows), then wave 0 adds the 16 wave sums in
+// wave order, so the result does not depend on timing.
+constexpr int kNormDwThreads = 1024;
+__global__ __launch_bounds__(kNormDwThreads) void rmsnorm_dw_kernel(const float* __restrict__ part,
+                                                                    float* __restrict__ dw,
+                                                                    int n, int n_rows) {
+  constexpr int kWaves = kNormDwThreads / 64;
+  __shared__ float sums[kNormDwThreads];
   const int wave = threadIdx.x >> 6;
   const int j = blockIdx.x * 64 + (threadIdx.x & 63);
   float s = 0.f;
   if (j < n) {
-#pragma unroll 8
-    for (int g = wave; g < n_rows; g += kNormThreads / 64) s += part[(size_t)g * n + j];
+#pragma unroll 16
+    for (int g = wave; g < n_rows; g += kWaves) s += part[(size_t)g * n + j];
   }
   sums[threadIdx.x] = s;
   __syncthreads();
   if (wave == 0 && j < n) {
     float t = sums[threadIdx.x];
 #pragma unroll
-    for (int w = 1; w < kNormThreads / 64; ++w) t += sums[threadIdx.x + 64 * w];
+    for (int w = 1; w < kWaves; ++w) t += sums[threadIdx.x + 64 * w];
     dw[j] = t;
   }
 }
@@ -217,7 +296,13 @@ hipError_t launch_fwd_lpr(const NormParams& p, hipStream_t stream) {
 
 template <int LPR>
 hipError_t launch_bwd_lpr(const NormParams& p, int n_wgs, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel<LPR>, dim3(n_wgs), dim3(kNormBwdThreads), 0, stream, p);
+  // A lane holds at most ceil(pieces / LPR) pieces: two below LPR = 64 (see
+  // pieces_per_lane), and with LPR = 64 two up to n = 1024, four above.
+  if (LPR < 64 || p.pieces <= 2 * LPR)
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<LPR, 2>), dim3(n_wgs), dim3(kNormBwdThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<LPR, pieces_per_lane<LPR>()>), dim3(n_wgs),
+                       dim3(kNormBwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -269,7 +354,7 @@ hipError_t launch_rmsnorm_bwd(const NormArgs& a, hipStream_t stream) {
     default: e = launch_bwd_lpr<64>(p, n_wgs, stream); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rmsnorm_dw_kernel, dim3((a.n + 63) / 64), dim3(kNormThreads), 0, stream,
+  hipLaunchKernelGGL(rmsnorm_dw_kernel, dim3((a.n + 63) / 64), dim3(kNormDwThreads), 0, stream,
                      (const float*)a.part, a.dw, a.n, n_wgs);
   return hipGetLastError();
 }
