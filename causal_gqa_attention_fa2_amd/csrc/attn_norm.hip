@@ -65,13 +65,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_fwd_kernel(NormParams p)
   const int row = (blockIdx.x * (kNormThreads / 64) + threadIdx.x / 64) * RPW + lane / LPR;
   if (row >= p.rows) return;  // whole groups leave together; no cross-group exchange follows
   const h16x8* xr = p.x + (size_t)row * p.pieces;
-  h16x8 xv[PPL];
-  float ss = 0.f;
+  // w goes out with x, so its latency hides under the row's.
+  h16x8 xv[PPL], wv[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; ++k) {
     const int c = gl + k * LPR;
     if (c < p.pieces) {
       xv[k] = xr[c];
+      wv[k] = p.w[c];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    const int c = gl + k * LPR;
+    if (c < p.pieces) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += (float)xv[k][e] * (float)xv[k][e];
     }
@@ -83,10 +91,9 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_fwd_kernel(NormParams p)
   for (int k = 0; k < PPL; ++k) {
     const int c = gl + k * LPR;
     if (c < p.pieces) {
-      const h16x8 wv = p.w[c];
       h16x8 o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (h16)((float)xv[k][e] * r * (float)wv[e]);
+      for (int e = 0; e < 8; ++e) o[e] = (h16)((float)xv[k][e] * r * (float)wv[k][e]);
       yr[c] = o;
     }
   }
