@@ -17,9 +17,12 @@ from oracle import rmsnorm_bwd_ref, rmsnorm_fwd_ref
 pytestmark = pytest.mark.gpu
 
 # (rows, n): every lane-group width (8, 16, 32, 64 lanes per row), ragged
-# piece counts, one row, and the widest supported row.
+# piece counts, one row, and the widest supported row. The last two give the
+# backward's row groups one or two rows (more rows than one grid stride of
+# 256 work-groups x 16 groups, not a multiple of it), so the loads of a
+# group's next row are issued for some groups and not for others.
 CASES = [(1, 8), (3, 64), (5, 96), (17, 128), (33, 1024), (7, 2048), (1000, 136), (300, 520),
-         (4099, 256)]
+         (4099, 256), (4500, 1024), (5000, 520)]
 
 
 def _run(inp, device):
