@@ -178,6 +178,7 @@ attn_status attn_fwd(const attn_varlen_dims* dims, const void* q, const void* k,
   a.h_kv = dims->h_kv;
   a.head_dim = dims->head_dim;
   a.scale = scale;
+  a.num_cus = num_compute_units();
   return cgqa::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -448,6 +449,7 @@ static attn_status prefill_impl(const attn_prefill_dims* dims, const void* q, co
   a.h_kv = dims->paged.h_kv;
   a.head_dim = dims->paged.head_dim;
   a.scale = scale;
+  a.num_cus = num_compute_units();
   return cgqa::launch_prefill(a, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -1059,7 +1059,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
-  const dim3 gq(n_items < a.num_cus ? n_items : a.num_cus);  // persistent dq grids
+  // Persistent dq grids; items are dealt by their residue mod 8, so the grid
+  // is the item count or at least 8.
+  const int resident = a.num_cus > 8 ? a.num_cus : 8;
+  const dim3 gq(n_items < resident ? n_items : resident);
   const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
   const long long wgs = (long long)((a.total_tokens + kRowsTB - 1) / kRowsTB) *
                         ((a.h_q + kRowsHC - 1) / kRowsHC);  // row-term tiles

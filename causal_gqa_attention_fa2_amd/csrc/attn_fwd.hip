@@ -9,12 +9,13 @@
 // LSE = m + ln l for the backward pass. FP16 inputs, FP32 accumulation
 // (pitchhut "Key Features", item 1).
 //
-// Work decomposition. One work-group of W waves per (sequence, query tile,
-// KV head, head chunk): hpw heads of the KV head's group times 32 * W / hpw
-// query positions, one wave per (head, 32 positions). For the usual group
-// sizes (1, 2, 4, 8) there is one chunk, so every K/V tile is read from HBM
-// once per work-group and shared by its G heads through LDS (grouped-query
-// sharing).
+// Work decomposition. An item is one (sequence, query tile, KV head, head
+// chunk): hpw heads of the KV head's group times 32 * W / hpw query
+// positions, one wave per (head, 32 positions), on a work-group of W waves.
+// For the usual group sizes (1, 2, 4, 8) there is one chunk, so every K/V
+// tile is read from HBM once per item and shared by its G heads through LDS
+// (grouped-query sharing). Work-groups are persistent: as many as stay
+// resident, each walking its share of the items heaviest first.
 //
 // Two shapes, chosen from the batch's dims (launch_fwd_impl):
 //   W = 8 (long sequences): eight waves, two per SIMD, share each K/V tile;
@@ -23,7 +24,7 @@
 //     compute of tiles t and t+1 to arrive. One work-group per CU.
 //   W = 4 (sequences up to 4096): four waves and a two-stage ring (64 KB),
 //     copies of tile t+1 issued at tile t, so two independent work-groups
-//     share each CU: one's prologue, epilogue and barrier waits overlap the
+//     share each CU: one's item start, end and barrier waits overlap the
 //     other's tiles, and the two waves of a SIMD are not tied to one barrier.
 // Either way one barrier per tile. K is stored with the
 // row-read chunk swizzle and V with the transpose-read swizzle (cdna4.h), so
@@ -75,6 +76,7 @@ struct FwdParams {
   // Ragged batches: 1 when work-groups walk the list of non-empty query tiles
   // (varlen_item) instead of every (query tile, sequence) slot.
   int mapped;
+  int n_items;       // items: slots (or list entries) times h_kv * n_chunks
   float scale_log2;  // scale * log2(e)
 };
 
@@ -91,15 +93,20 @@ constexpr int kMapSeqs = 64 * kMapChunks;
 //   nt_b = ceil(L_b / BR) (at most n_qtiles), A(t) = sum_b max(nt_b - t, 0)
 //   is the number of items with tile index >= t, so item k has the largest
 //   qt with A(qt) > k, and is the (k - A(qt + 1))-th sequence with nt_b > qt.
-__device__ __forceinline__ bool varlen_item(const FwdParams& p, int k, int lane, int BR, int& qt,
-                                            int& b) {
-  int nt[kMapChunks];
+// nt_b of the sequences lane + 64c (zero past the batch), loaded once per
+// work-group.
+__device__ __forceinline__ void varlen_counts(const FwdParams& p, int lane, int BR,
+                                              int (&nt)[kMapChunks]) {
 #pragma unroll
   for (int c = 0; c < kMapChunks; ++c) {
     const int bb = lane + 64 * c;
     nt[c] = 0;
     if (bb < p.n_seqs) nt[c] = min((p.cu[bb + 1] - p.cu[bb] + BR - 1) / BR, p.n_qtiles);
   }
+}
+
+__device__ __forceinline__ bool varlen_item(const FwdParams& p, const int (&nt)[kMapChunks], int k,
+                                            int lane, int& qt, int& b) {
   // A(t) for t = lane + 64 j, by broadcasting each nt_b.
   int cnt = 0;       // tiles t with A(t) > k
   int a_next = 0;    // A(qt + 1), found below
@@ -165,39 +172,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
   __shared__ __attribute__((aligned(16))) f16 Vs[NS][kBC * D];
 
   const int BR = 32 * p.nqb;
-  // Heaviest query tiles (the last ones of the longest sequences) first.
   // Work-group and lane ids come straight from the hardware registers: this
   // file is built without IEEE mode, so device-library helpers (compiled
   // with it) are not inlined here and none may be called.
-  const int wg = (int)__builtin_amdgcn_workgroup_id_x();
   const int hc = p.h_kv * p.n_chunks;
-  const int chunk = (wg % hc) % p.n_chunks;
-  const int g = (wg % hc) / p.n_chunks;
-  int qt, b;
-  if (p.mapped) {
-    // Ragged batch: work-group w takes item w / hc of the list of non-empty
-    // query tiles (work-groups past its end exit).
-    if (!varlen_item(p, wg / hc, (int)__builtin_amdgcn_workitem_id_x() & 63, BR, qt, b)) return;
-    qt = __builtin_amdgcn_readfirstlane(qt);
-    b = __builtin_amdgcn_readfirstlane(b);
-  } else {
-    // Every (query tile, sequence) slot, tile index descending.
-    qt = p.n_qtiles - 1 - wg / (p.n_seqs * hc);
-    b = (wg % (p.n_seqs * hc)) / hc;
-  }
-  const int s0 = p.cu[b];
-  const int L = p.cu[b + 1] - s0;  // queries of the sequence
-  const int q_wg0 = qt * BR;
-  if (q_wg0 >= L) return;  // uniform over the work-group
-  // off: position of the sequence's first query; Lk: its number of keys.
-  int off = 0, Lk = L;
-  if constexpr (PAGED) {
-    Lk = min(p.ctx[b], p.max_ctx);  // a context past the table is clamped
-    if (Lk < L) return;  // invalid batch (a chunk longer than its context)
-    off = Lk - L;
-  }
-  const int n_kt = (off + min(L, q_wg0 + BR) + kBC - 1) / kBC;
-
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
@@ -205,29 +183,25 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
   const int hi = lane >> 5;
   const int grp = lane >> 4;
   const int j16 = lane & 15;
-  const int hig = chunk * p.hpw + wave / p.nqb;  // head within the group
-  const int head = g * p.G + min(hig, p.G - 1);
-  const int q0 = q_wg0 + (wave % p.nqb) * 32;  // first query row of the wave
-  const int qpos = q0 + l32;                    // this lane's query row
-  const int q0a = off + q0;                     // their context positions
-  const int qposa = off + qpos;
-  const bool wave_has_rows = q0 < L && hig < p.G;
-  const bool qvalid = qpos < L && hig < p.G;
 
-  // Copy of K/V tile kt into ring stage `stage`: instruction i of this wave
-  // fills rows (wave * IPW + i) * RPI + lane / CH; lane l lands in chunk slot
-  // l % CH of its row and fetches the global chunk that the swizzle maps
-  // there. Keys past the sequence fetch its last row: their scores are
-  // masked and their weights are zero. In the paged case the RPI rows of one
-  // instruction lie in one 16-token block (RPI divides 16), so its physical
-  // block is one wave-uniform scalar load; out-of-range table entries are
-  // clamped into the pool, so no access leaves it.
-  // Packed keys and values: the tile's first row is a wave-uniform base in
-  // SGPRs and each lane adds a 32-bit byte offset fixed for the kernel
-  // (recomputed with the clamp only on the sequence's last tile).
-  // Paged keys and values: the RPI rows of one copy instruction lie in one
-  // 16-token block, so the base is that instruction's first row and the
-  // lane's row is lane / CH rows further (clamped like the row itself).
+  // Persistent work-groups walk the items: item i is the (query tile,
+  // sequence) slot i / hc (or entry i / hc of the list of non-empty query
+  // tiles of a ragged batch), KV head and head chunk from i % hc; slots and
+  // list run heaviest first. As in the dq kernel, work-group w on XCD
+  // x = w % 8 takes only items x + 8j (the query tiles of one (sequence, KV
+  // head) then share one L2), in snake order over that XCD's work-groups.
+  // Staying resident, a work-group starts its next item while the stores of
+  // the last one drain, and the ragged list's tile counts load once.
+  constexpr int kXcds = 8;
+  const int NW = (int)__builtin_amdgcn_readfirstlane((int)gridDim.x);
+  const int wgi = (int)__builtin_amdgcn_workgroup_id_x();
+  const int xcd = wgi % kXcds;
+  const int wx = wgi / kXcds;
+  const int nwx = (NW - xcd + kXcds - 1) / kXcds;  // groups on this XCD
+  int nt[kMapChunks];
+  if (p.mapped) varlen_counts(p, lane, BR, nt);
+
+  // Copy offsets (fixed per lane for every item) and LDS bases.
   auto copy_off = [&](int i, int last, bool tr) {
     const int r = (wave * IPW + i) * RPI + lane / CH;
     const int col = tr ? swz_tr<D>(r, (lane % CH) * 8) : swz<D>(r, (lane % CH) * 8);
@@ -241,71 +215,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
     voffc[i] = copy_off(i, PAGED ? RPI - 1 : kBC - 1, true);
   }
   const uint32_t ks_lds = lds_addr(&Ks[0][0]), vs_lds = lds_addr(&Vs[0][0]);
-  auto issue_tile = [&](int kt, int stage) {
-    // One branch per tile (not per copy) between the fixed offsets and, on
-    // the sequence's last tile, the clamped ones.
-    if constexpr (PAGED) {
-      auto copies = [&](bool tail) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-          const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
-          const int lb = min(t0 >> 4, p.max_blocks - 1);
-          const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
-          const size_t base = ((size_t)(phys * 16 + (t0 - (lb << 4))) * p.h_kv + g) * D;
-          const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
-          dma16s_at(p.k + base, tail ? copy_off(i, Lk - 1 - t0, false) : koffc[i], ks_lds + dst);
-          dma16s_at(p.v + base, tail ? copy_off(i, Lk - 1 - t0, true) : voffc[i], vs_lds + dst);
-        }
-      };
-      if (kt * kBC + kBC > Lk) copies(true);  // wave-uniform
-      else copies(false);
-    } else {
-      const int k0 = kt * kBC;
-      const size_t base = ((size_t)(s0 + k0) * p.h_kv + g) * D;
-      auto copies = [&](bool tail) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-          const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
-          dma16s_at(p.k + base, tail ? copy_off(i, L - 1 - k0, false) : koffc[i], ks_lds + dst);
-          dma16s_at(p.v + base, tail ? copy_off(i, L - 1 - k0, true) : voffc[i], vs_lds + dst);
-        }
-      };
-      if (k0 + kBC > L) copies(true);  // wave-uniform
-      else copies(false);
-    }
-  };
-
-  // The first tile's copies go out before the Q loads below, so the two
-  // latencies overlap instead of adding up.
-  issue_tile(0, 0);
-
-  // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7]. Rows past the
-  // sequence read its last row (loads stay unconditional) and are never stored.
-  f16x8 qf[NT];
-  {
-    const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
-  }
-  if constexpr (ROPE) {
-    // Dimension 16t + 8hi + e (t < NT/2) pairs with the one D/2 further,
-    // which is element e of fragment t + NT/2 of the same lane.
-    const int pos = min(off + min(qpos, L - 1), p.max_pos - 1);
-    const float* ct = p.cos_t + (size_t)pos * (D / 2) + 8 * hi;
-    const float* st = p.sin_t + (size_t)pos * (D / 2) + 8 * hi;
-#pragma unroll
-    for (int t = 0; t < NT / 2; ++t) rope_rotate8(qf[t], qf[t + NT / 2], ct + 16 * t, st + 16 * t, 1.f);
-  }
-
-  f32x16 oacc[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) oacc[db] = zero_f32x16();
-  float m_run = kMaxInit;  // reference maximum of the scaled scores (log2 units)
-  float l_run = 0.f;       // this half-wave's share of the row sum
-
   // Per-lane LDS offsets (halves) of the operand reads, fixed for the whole
-  // loop: the chunk swizzles depend on the row only through row % 16 (K) and
-  // row % 4 (V), so the other rows of a lane's reads sit at constant
+  // kernel: the chunk swizzles depend on the row only through row % 16 (K)
+  // and row % 4 (V), so the other rows of a lane's reads sit at constant
   // distances and every read below is base + per-lane offset + immediate.
   int koff[NT];  // K row l32, columns 16t + 8hi (row 32 + l32: + 32 D)
 #pragma unroll
@@ -317,152 +229,270 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
     voff[db] = r * D + swz_tr<D>(r, 32 * db + 16 * (grp & 1) + 4 * (j16 & 3));
   }
 
-  // One tile step on ring stage S = kt % NS (a compile-time constant).
-  // Three stages: the copies of tile kt + 2 go to stage (S + 2) % 3, which
-  // held tile kt - 1. Two stages: those of tile kt + 1 go to stage
-  // (S + 1) % 2, which held tile kt - 1.
-  auto step = [&](int kt, auto S) {
-    constexpr int stage = decltype(S)::value;
-    // Tile kt has landed (this wave's copies; with three stages tile
-    // kt + 1's may still fly), then every wave's copies have, and every wave
-    // is done with tile kt - 1.
-    if constexpr (NS == 3) {
-      if (kt + 1 < n_kt) wait_vm_barrier<2 * IPW>();
-      else wait_vm_barrier<0>();
-      if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % NS);
+  for (int round = 0;; ++round) {
+    const int item = xcd + kXcds * (round * nwx + ((round & 1) ? nwx - 1 - wx : wx));
+    if (item >= p.n_items) break;  // uniform; later rounds only go further
+    const int chunk = (item % hc) % p.n_chunks;
+    const int g = (item % hc) / p.n_chunks;
+    int qt, b;
+    if (p.mapped) {
+      if (!varlen_item(p, nt, item / hc, lane, qt, b)) continue;  // past the list's end
+      qt = __builtin_amdgcn_readfirstlane(qt);
+      b = __builtin_amdgcn_readfirstlane(b);
     } else {
-      wait_vm_barrier<0>();
-      if (kt + 1 < n_kt) issue_tile(kt + 1, (stage + 1) % NS);
+      // Every (query tile, sequence) slot, tile index descending.
+      qt = p.n_qtiles - 1 - item / (p.n_seqs * hc);
+      b = (item % (p.n_seqs * hc)) / hc;
+    }
+    const int s0 = load_uniform(p.cu, b);
+    const int L = load_uniform(p.cu, b + 1) - s0;  // queries of the sequence
+    const int q_wg0 = qt * BR;
+    if (q_wg0 >= L) continue;  // uniform over the work-group
+    // off: position of the sequence's first query; Lk: its number of keys.
+    int off = 0, Lk = L;
+    if constexpr (PAGED) {
+      Lk = min(load_uniform(p.ctx, b), p.max_ctx);  // a context past the table is clamped
+      if (Lk < L) continue;  // invalid batch (a chunk longer than its context)
+      off = Lk - L;
+    }
+    const int n_kt = (off + min(L, q_wg0 + BR) + kBC - 1) / kBC;
+
+    const int hig = chunk * p.hpw + wave / p.nqb;  // head within the group
+    const int head = g * p.G + min(hig, p.G - 1);
+    const int q0 = q_wg0 + (wave % p.nqb) * 32;  // first query row of the wave
+    const int qpos = q0 + l32;                    // this lane's query row
+    const int q0a = off + q0;                     // their context positions
+    const int qposa = off + qpos;
+    const bool wave_has_rows = q0 < L && hig < p.G;
+    const bool qvalid = qpos < L && hig < p.G;
+
+    // Copy of K/V tile kt into ring stage `stage`: instruction i of this wave
+    // fills rows (wave * IPW + i) * RPI + lane / CH; lane l lands in chunk
+    // slot l % CH of its row and fetches the global chunk that the swizzle
+    // maps there. Keys past the sequence fetch its last row: their scores
+    // are masked and their weights are zero. In the paged case the RPI rows
+    // of one instruction lie in one 16-token block (RPI divides 16), so its
+    // physical block is one wave-uniform scalar load; out-of-range table
+    // entries are clamped into the pool, so no access leaves it.
+    // Packed keys and values: the tile's first row is a wave-uniform base in
+    // SGPRs and each lane adds a 32-bit byte offset fixed for the kernel
+    // (recomputed with the clamp only on the sequence's last tile).
+    // Paged keys and values: the RPI rows of one copy instruction lie in one
+    // 16-token block, so the base is that instruction's first row and the
+    // lane's row is lane / CH rows further (clamped like the row itself).
+    auto issue_tile = [&](int kt, int stage) {
+      // One branch per tile (not per copy) between the fixed offsets and, on
+      // the sequence's last tile, the clamped ones.
+      if constexpr (PAGED) {
+        auto copies = [&](bool tail) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < IPW; ++i) {
+            const int t0 = min(kt * kBC + (wave * IPW + i) * RPI, Lk - 1);  // wave-uniform
+            const int lb = min(t0 >> 4, p.max_blocks - 1);
+            const int phys = min(max(load_uniform(p.bt, b * p.max_blocks + lb), 0), p.num_blocks - 1);
+            const size_t base = ((size_t)(phys * 16 + (t0 - (lb << 4))) * p.h_kv + g) * D;
+            const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+            dma16s_at(p.k + base, tail ? copy_off(i, Lk - 1 - t0, false) : koffc[i], ks_lds + dst);
+            dma16s_at(p.v + base, tail ? copy_off(i, Lk - 1 - t0, true) : voffc[i], vs_lds + dst);
+          }
+        };
+        if (kt * kBC + kBC > Lk) copies(true);  // wave-uniform
+        else copies(false);
+      } else {
+        const int k0 = kt * kBC;
+        const size_t base = ((size_t)(s0 + k0) * p.h_kv + g) * D;
+        auto copies = [&](bool tail) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < IPW; ++i) {
+            const uint32_t dst = (uint32_t)(stage * kBC * D + (wave * IPW + i) * 64 * 8) * 2u;
+            dma16s_at(p.k + base, tail ? copy_off(i, L - 1 - k0, false) : koffc[i], ks_lds + dst);
+            dma16s_at(p.v + base, tail ? copy_off(i, L - 1 - k0, true) : voffc[i], vs_lds + dst);
+          }
+        };
+        if (k0 + kBC > L) copies(true);  // wave-uniform
+        else copies(false);
+      }
+    };
+
+    // The first tile's copies go out before the Q loads below, so the two
+    // latencies overlap instead of adding up.
+    issue_tile(0, 0);
+
+    // Q^T as the B operand: lane holds Q[qpos][16t + 8hi .. +7]. Rows past
+    // the sequence read its last row (loads stay unconditional) and are never
+    // stored.
+    f16x8 qf[NT];
+    {
+      const f16* qrow = p.q + ((size_t)(s0 + min(qpos, L - 1)) * p.h_q + head) * D + 8 * hi;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) qf[t] = *(const f16x8*)(qrow + 16 * t);
+    }
+    if constexpr (ROPE) {
+      // Dimension 16t + 8hi + e (t < NT/2) pairs with the one D/2 further,
+      // which is element e of fragment t + NT/2 of the same lane.
+      const int pos = min(off + min(qpos, L - 1), p.max_pos - 1);
+      const float* ct = p.cos_t + (size_t)pos * (D / 2) + 8 * hi;
+      const float* st = p.sin_t + (size_t)pos * (D / 2) + 8 * hi;
+#pragma unroll
+      for (int t = 0; t < NT / 2; ++t) rope_rotate8(qf[t], qf[t + NT / 2], ct + 16 * t, st + 16 * t, 1.f);
     }
 
-    if (!wave_has_rows || kt * kBC > q0a + 31) return;  // fully masked for this wave
-    const f16* Kb = Ks[stage];
-    const f16* Vb = Vs[stage];
-    // S^T for the two 32-key halves of the tile, as two interleaved chains.
-    // Every K fragment of the tile is read in one batch before the products
-    // (scheduling fences keep the compiler from pairing each read with its
-    // use, which left the matrix core waiting on LDS latency), and the V^T
-    // fragments go out right behind them, so they land during the softmax.
-    f32x16 s[2] = {zero_f32x16(), zero_f32x16()};
-    {
-      f16x8 kf[2][NT];
+    f32x16 oacc[ND];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        kf[0][t] = *(const f16x8*)(Kb + koff[t]);
-        kf[1][t] = *(const f16x8*)(Kb + 32 * D + koff[t]);
+    for (int db = 0; db < ND; ++db) oacc[db] = zero_f32x16();
+    float m_run = kMaxInit;  // reference maximum of the scaled scores (log2 units)
+    float l_run = 0.f;       // this half-wave's share of the row sum
+    // One tile step on ring stage S = kt % NS (a compile-time constant).
+    // Three stages: the copies of tile kt + 2 go to stage (S + 2) % 3, which
+    // held tile kt - 1. Two stages: those of tile kt + 1 go to stage
+    // (S + 1) % 2, which held tile kt - 1.
+    auto step = [&](int kt, auto S) {
+      constexpr int stage = decltype(S)::value;
+      // Tile kt has landed (this wave's copies; with three stages tile
+      // kt + 1's may still fly), then every wave's copies have, and every wave
+      // is done with tile kt - 1.
+      if constexpr (NS == 3) {
+        if (kt + 1 < n_kt) wait_vm_barrier<2 * IPW>();
+        else wait_vm_barrier<0>();
+        if (kt + 2 < n_kt) issue_tile(kt + 2, (stage + 2) % NS);
+      } else {
+        wait_vm_barrier<0>();
+        if (kt + 1 < n_kt) issue_tile(kt + 1, (stage + 1) % NS);
+      }
+
+      if (!wave_has_rows || kt * kBC > q0a + 31) return;  // fully masked for this wave
+      const f16* Kb = Ks[stage];
+      const f16* Vb = Vs[stage];
+      // S^T for the two 32-key halves of the tile, as two interleaved chains.
+      // Every K fragment of the tile is read in one batch before the products
+      // (scheduling fences keep the compiler from pairing each read with its
+      // use, which left the matrix core waiting on LDS latency), and the V^T
+      // fragments go out right behind them, so they land during the softmax.
+      f32x16 s[2] = {zero_f32x16(), zero_f32x16()};
+      {
+        f16x8 kf[2][NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          kf[0][t] = *(const f16x8*)(Kb + koff[t]);
+          kf[1][t] = *(const f16x8*)(Kb + 32 * D + koff[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          s[0] = mfma32x32x16(kf[0][t], qf[t], s[0]);
+          s[1] = mfma32x32x16(kf[1][t], qf[t], s[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f16x8 vf[4][ND];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          vf[u][db] = cat4(lds_read_tr(Vb + voff[db] + 16 * u * D),
+                           lds_read_tr(Vb + voff[db] + (16 * u + 8) * D));
       }
       __builtin_amdgcn_sched_barrier(0);
+      // Causal mask (diagonal tiles only) and the tile maximum of raw scores.
+      if (kt * kBC + kBC - 1 > q0a) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s[0] = mfma32x32x16(kf[0][t], qf[t], s[0]);
-        s[1] = mfma32x32x16(kf[1][t], qf[t], s[1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    f16x8 vf[4][ND];
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-        vf[u][db] = cat4(lds_read_tr(Vb + voff[db] + 16 * u * D),
-                         lds_read_tr(Vb + voff[db] + (16 * u + 8) * D));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Causal mask (diagonal tiles only) and the tile maximum of raw scores.
-    if (kt * kBC + kBC - 1 > q0a) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt * kBC + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key > qposa) s[kb][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt * kBC + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (key > qposa) s[kb][i] = -INFINITY;
+          }
         }
       }
-    }
-    // Two independent three-input max chains (v_max3_f32) over the 32 scores.
-    float mx0 = fmaxf(s[0][0], s[1][0]), mx1 = fmaxf(s[0][1], s[1][1]);
+      // Two independent three-input max chains (v_max3_f32) over the 32 scores.
+      float mx0 = fmaxf(s[0][0], s[1][0]), mx1 = fmaxf(s[0][1], s[1][1]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][i]), s[1][i]);
-      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[0][i + 1]), s[1][i + 1]);
+      for (int i = 2; i < 16; i += 2) {
+        mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][i]), s[1][i]);
+        mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[0][i + 1]), s[1][i + 1]);
+      }
+      float mx = fmaxf(mx0, mx1);
+      mx = half_swap_max(mx) * p.scale_log2;
+      // m_run is a reference point, not always the exact running maximum: it
+      // moves (and O and l are rescaled) only when a row's maximum passes it by
+      // more than kLazy, so the weights below stay <= 2^kLazy and the wave
+      // skips the rescale in almost every tile after the first. The result is
+      // the same softmax up to rounding, whatever the reference.
+      const bool grow = mx > m_run + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float m_new = m_run;
+
+      // P^T = exp2(S^T * scale * log2(e) - m), as B operands: k-step u covers
+      // tile keys 16u..16u+15; slot e of half hi holds key 16u + 8(e/4) +
+      // 4hi + e%4.
+      f16x8 pf[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + e], p.scale_log2, -m_new));
+          rs += x;
+          pf[u][e] = (f16)x;
+        }
+      }
+      l_run += rs;
+
+      // O^T += V^T P^T. A-operand slot e of half hi must hold V[key(e)][d]
+      // for the same keys: transpose reads (above) of rows 16u + 4hi + j16/4
+      // and 8 rows further. The k-step loop is outermost, so consecutive
+      // products go to different accumulators (four independent chains).
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] = mfma32x32x16(vf[u][db], pf[u], oacc[db]);
+      }
+    };
+
+    // Q^T was loaded with ordinary loads: wait for them here with the builtin
+    // (whose effect the compiler tracks), so it places no wait of its own inside
+    // the loop, where such a wait would also stall on the copies in flight.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0); tile 0 included
+    if (NS == 3 && n_kt > 1) issue_tile(1, 1);
+    for (int kt = 0; kt < n_kt; kt += NS) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
+      if constexpr (NS == 3) {
+        if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
+      }
     }
-    float mx = fmaxf(mx0, mx1);
-    mx = half_swap_max(mx) * p.scale_log2;
-    // m_run is a reference point, not always the exact running maximum: it
-    // moves (and O and l are rescaled) only when a row's maximum passes it by
-    // more than kLazy, so the weights below stay <= 2^kLazy and the wave
-    // skips the rescale in almost every tile after the first. The result is
-    // the same softmax up to rounding, whatever the reference.
-    const bool grow = mx > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
+
+    const float l_tot = half_swap_sum(l_run);  // all lanes take part in the exchange
+    if (qvalid) {
+      const float inv = 1.f / l_tot;
+      f16* orow = p.o + ((size_t)(s0 + qpos) * p.h_q + head) * D;
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (f16)(oacc[db][4 * r4 + e] * inv);
+          *(f16x4*)(orow + 32 * db + 8 * r4 + 4 * hi) = w;
+        }
       }
-      m_run = m_new;
+      if (hi == 0 && (!PAGED || p.lse != nullptr))
+        p.lse[(size_t)head * p.T + s0 + qpos] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
-    const float m_new = m_run;
-
-    // P^T = exp2(S^T * scale * log2(e) - m), as B operands: k-step u covers
-    // tile keys 16u..16u+15; slot e of half hi holds key 16u + 8(e/4) +
-    // 4hi + e%4.
-    f16x8 pf[4];
-    float rs = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + e], p.scale_log2, -m_new));
-        rs += x;
-        pf[u][e] = (f16)x;
-      }
-    }
-    l_run += rs;
-
-    // O^T += V^T P^T. A-operand slot e of half hi must hold V[key(e)][d]
-    // for the same keys: transpose reads (above) of rows 16u + 4hi + j16/4
-    // and 8 rows further. The k-step loop is outermost, so consecutive
-    // products go to different accumulators (four independent chains).
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db) oacc[db] = mfma32x32x16(vf[u][db], pf[u], oacc[db]);
-    }
-  };
-
-  // Q^T was loaded with ordinary loads: wait for them here with the builtin
-  // (whose effect the compiler tracks), so it places no wait of its own inside
-  // the loop, where such a wait would also stall on the copies in flight.
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0); tile 0 included
-  if (NS == 3 && n_kt > 1) issue_tile(1, 1);
-  for (int kt = 0; kt < n_kt; kt += NS) {
-    step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
-    if constexpr (NS == 3) {
-      if (kt + 2 < n_kt) step(kt + 2, std::integral_constant<int, 2>{});
-    }
+    // Every wave is done with the ring before the next item's copies land in
+    // it (an LDS-only barrier: the stores above stay in flight).
+    lds_barrier();
   }
-
-  const float l_tot = half_swap_sum(l_run);  // all lanes take part in the exchange
-  if (!qvalid) return;
-  const float inv = 1.f / l_tot;
-  f16* orow = p.o + ((size_t)(s0 + qpos) * p.h_q + head) * D;
-#pragma unroll
-  for (int db = 0; db < ND; ++db) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (f16)(oacc[db][4 * r4 + e] * inv);
-      *(f16x4*)(orow + 32 * db + 8 * r4 + 4 * hi) = w;
-    }
-  }
-  if (hi == 0 && (!PAGED || p.lse != nullptr))
-    p.lse[(size_t)head * p.T + s0 + qpos] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -526,7 +556,12 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   const long long items = std::min<long long>(slots, (long long)a.total_tokens / BR + a.n_seqs);
   p.mapped = items < slots && a.n_seqs <= kMapSeqs &&
              (long long)a.n_seqs * ((p.n_qtiles + 63) / 64) <= 512;
-  const dim3 grid((unsigned)((p.mapped ? items : slots) * a.h_kv * p.n_chunks));
+  // Persistent grid: at most one work-group per CU (eight waves) or two
+  // (four waves), each walking its share of the items. Items are dealt by
+  // their residue mod 8, so the grid is the item count or at least 8.
+  p.n_items = (int)((p.mapped ? items : slots) * a.h_kv * p.n_chunks);
+  const int resident = std::max((W == 4 ? 2 : 1) * a.num_cus, 8);
+  const dim3 grid((unsigned)std::max(1, std::min(p.n_items, resident)));
   if (W == 4)
     launch_fwd_shape<PAGED, 4>(p, a, grid, stream);
   else

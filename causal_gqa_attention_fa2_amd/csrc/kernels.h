@@ -29,6 +29,7 @@ struct FwdArgs {
   int rope_max_pos = 0;
   int n_seqs, total_tokens, max_seqlen, h_q, h_kv, head_dim;
   float scale;
+  int num_cus = 256;  // compute units of the device (persistent grid size)
 };
 
 // New keys and values of a chunked prefill, written into the paged pools.
