@@ -48,6 +48,8 @@
 #include "cdna4.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 #include <type_traits>
 
 namespace cgqa {
@@ -84,6 +86,10 @@ struct BwdParams {
   const float* __restrict__ sin_t;
   int max_pos;
   int n_seqs, T, h_q, h_kv, G, hpw, nqb, n_chunks, n_qtiles, n_ktiles;
+  // Ragged batches: 1 when dK/dV work-groups walk the list of non-empty key
+  // tiles sorted by work (dkdv_item) instead of every (key tile, sequence)
+  // slot; max_qb bounds a key tile's query blocks.
+  int kmapped, max_qb;
   float scale, scale_log2;
 };
 
@@ -433,6 +439,72 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   }
 }
 
+// Item k of the list of a ragged batch's non-empty key tiles, heaviest
+// first: the pairs (sequence b, key tile kt) with kt < nk_b = ceil(L_b / 128),
+// ordered by their work w = c_b - 4 kt descending (c_b = ceil(L_b / 32) query
+// blocks; the tile sees the blocks from 4 kt on), then by b. With the
+// work-groups dispatched in this order, the longest tiles start first and
+// the shortest fill the end. Every wave computes the same answer from
+// cu_seqlens; lane l holds the sequences l + 64c. Returns false past the end.
+//   A(v) = sum_b #{kt < nk_b : c_b - 4 kt >= v} = sum_b min(nk_b, (c_b - v) / 4 + 1)
+//   (0 when c_b < v) counts the items of work >= v, so item k has the largest
+//   work v* with A(v*) > k, and is the (k - A(v* + 1))-th sequence, by b, with
+//   a tile of work exactly v*: (c_b - v*) % 4 == 0 and (c_b - v*) / 4 < nk_b.
+constexpr int kKMapChunks = 4;  // up to 256 sequences
+__device__ __forceinline__ bool dkdv_item(const BwdParams& p, int k, int lane, int& b, int& kt) {
+  int cq[kKMapChunks], nk[kKMapChunks];
+#pragma unroll
+  for (int c = 0; c < kKMapChunks; ++c) {
+    const int bb = lane + 64 * c;
+    const int len = bb < p.n_seqs ? p.cu[bb + 1] - p.cu[bb] : 0;
+    cq[c] = (len + 31) / 32;
+    nk[c] = (len + kBK - 1) / kBK;
+  }
+  int cnt = 0;     // works v in 1 .. max_qb with A(v) > k
+  int a_next = 0;  // A(cnt + 1), found below
+  const int nj = (p.max_qb + 63) >> 6;
+  for (int j = 0; j < nj; ++j) {
+    const int v = 1 + lane + 64 * j;
+    int a = 0;
+#pragma unroll
+    for (int c = 0; c < kKMapChunks; ++c) {
+      if (64 * c >= p.n_seqs) break;  // uniform
+      const int nb = min(p.n_seqs - 64 * c, 64);
+      for (int i = 0; i < nb; ++i) {
+        const int cb = __builtin_amdgcn_readlane(cq[c], i);
+        const int kb = __builtin_amdgcn_readlane(nk[c], i);
+        if (cb >= v) a += min(kb, (cb - v) / 4 + 1);
+      }
+    }
+    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v <= p.max_qb && a > k));
+    // A is non-increasing in v, so the works with A(v) > k are 1 .. cnt;
+    // A(cnt + 1) is this lane's value where v == cnt + 1.
+    const uint64_t m = __builtin_amdgcn_ballot_w64(v == cnt + 1);
+    if (m) a_next = __builtin_amdgcn_readlane(a, __builtin_ctzll(m));
+  }
+  if (cnt == 0) return false;  // k >= A(1), the number of items
+  const int vs = cnt;
+  int r = k - (vs < p.max_qb ? a_next : 0);
+#pragma unroll
+  for (int c = 0; c < kKMapChunks; ++c) {
+    const int d = cq[c] - vs;
+    const bool has = 64 * c + lane < p.n_seqs && d >= 0 && (d & 3) == 0 && (d >> 2) < nk[c];
+    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+    const int n = __builtin_popcountll(m);
+    if (r < n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint64_t sel = __builtin_amdgcn_ballot_w64(has && below == r);
+      const int src = __builtin_ctzll(sel);
+      b = 64 * c + src;
+      kt = __builtin_amdgcn_readlane(d, src) >> 2;
+      return true;
+    }
+    r -= n;
+  }
+  return false;
+}
+
 template <int D, bool STORE_DS, bool ROPE = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NT = D / 16;
@@ -453,11 +525,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) f16 Px[2][4][2 * 64 * 8];
 
   // Key tile 0 of every (sequence, KV head) sees the most query rows: first.
-  const int per = p.n_seqs * p.h_kv;
-  const int kt = (int)blockIdx.x / per;
-  const int rem = (int)blockIdx.x % per;
-  const int g = rem % p.h_kv;
-  const int b = rem / p.h_kv;
+  // Ragged batches walk the work-sorted list of non-empty key tiles.
+  int kt, g, b;
+  if (p.kmapped) {
+    g = (int)blockIdx.x % p.h_kv;
+    if (!dkdv_item(p, (int)blockIdx.x / p.h_kv, (int)threadIdx.x & 63, b, kt)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    kt = __builtin_amdgcn_readfirstlane(kt);
+  } else {
+    const int per = p.n_seqs * p.h_kv;
+    kt = (int)blockIdx.x / per;
+    const int rem = (int)blockIdx.x % per;
+    g = rem % p.h_kv;
+    b = rem / p.h_kv;
+  }
   const int s0 = p.cu[b];
   const int L = p.cu[b + 1] - s0;
   const int k_wg0 = kt * kBK;
@@ -1063,7 +1144,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   // is the item count or at least 8.
   const int resident = a.num_cus > 8 ? a.num_cus : 8;
   const dim3 gq(n_items < resident ? n_items : resident);
-  const dim3 gk(p.n_ktiles * a.n_seqs * a.h_kv);
+  // Ragged batches: the list of non-empty key tiles has at most
+  // floor(T / 128) + n_seqs entries (each sequence adds at most one partial
+  // tile), against n_ktiles * n_seqs slots.
+  const long long kslots = (long long)p.n_ktiles * a.n_seqs;
+  const long long kitems = std::min<long long>(kslots, (long long)a.total_tokens / kBK + a.n_seqs);
+  p.max_qb = (a.max_seqlen + 31) / 32;
+  p.kmapped = kitems < kslots && a.n_seqs <= 64 * kKMapChunks &&
+              (long long)a.n_seqs * ((p.max_qb + 63) / 64) <= 512;
+  const dim3 gk((unsigned)((p.kmapped ? kitems : kslots) * a.h_kv));
   const long long wgs = (long long)((a.total_tokens + kRowsTB - 1) / kRowsTB) *
                         ((a.h_q + kRowsHC - 1) / kRowsHC);  // row-term tiles
   const dim3 gr((unsigned)(wgs < 4 * a.num_cus ? wgs : 4 * a.num_cus));
