@@ -77,40 +77,62 @@ struct FwdParams {
   // (varlen_item) instead of every (query tile, sequence) slot.
   int mapped;
   int n_items;       // items: slots (or list entries) times h_kv * n_chunks
+  // List keys base_b + map_s * qt in 0 .. map_keys - 1, with base_b the
+  // cached context in units of map_unit = min(BR, 64) keys.
+  int map_unit, map_s, map_keys;
   float scale_log2;  // scale * log2(e)
 };
 
 // Largest batch the query-tile list handles: n_seqs <= kMapSeqs, and the
-// host also bounds n_seqs * ceil(n_qtiles / 64) (the cost of the list).
+// host also bounds n_seqs * ceil(map_keys / 64) (the cost of the list).
 constexpr int kMapChunks = 4;
 constexpr int kMapSeqs = 64 * kMapChunks;
 
-// Item k of the heaviest-first list of the batch's query tiles: the pairs
-// (sequence b, query tile qt) with qt * BR < L_b, ordered by qt descending
-// (the tiles with the most keys first), then by b. Every wave of the
-// work-group computes the same answer from cu_seqlens; lane l handles the
-// sequences l + 64c. Returns false when k is past the end of the list.
-//   nt_b = ceil(L_b / BR) (at most n_qtiles), A(t) = sum_b max(nt_b - t, 0)
-//   is the number of items with tile index >= t, so item k has the largest
-//   qt with A(qt) > k, and is the (k - A(qt + 1))-th sequence with nt_b > qt.
-// nt_b of the sequences lane + 64c (zero past the batch), loaded once per
-// work-group.
+// The list of a ragged batch's query tiles, heaviest first: the pairs
+// (sequence b, query tile qt) with qt * BR < L_b, ordered by the number of
+// keys they read, then by b. In units of u = min(BR, 64) keys that is
+// base_b + s qt + s (s = BR / u >= 1; base_b = ceil(off_b / u), the cached
+// context in the paged prefill, 0 for packed sequences), up to one less on
+// a sequence's partial last tile, so the list is sorted by
+// key_b(qt) = base_b + s qt.
+// Every wave of the work-group computes the same answer from cu_seqlens
+// (and the context lengths); lane l handles the sequences l + 64c.
+//   nt_b = ceil(L_b / BR) (at most n_qtiles) and
+//   A(t) = sum_b #{qt < nt_b : base_b + s qt >= t}
+//        = sum_b clamp(nt_b - ceil(max(t - base_b, 0) / s), 0, nt_b)
+//   counts the items with key >= t, so item k has the largest key t with
+//   A(t) > k, and is the (k - A(t + 1))-th sequence, by b, whose tiles
+//   include one with that key: t - base_b >= 0, divisible by s, and
+//   (t - base_b) / s < nt_b.
+// nt_b and base_b of the sequences lane + 64c (zero past the batch), loaded
+// once per work-group.
+template <bool PAGED>
 __device__ __forceinline__ void varlen_counts(const FwdParams& p, int lane, int BR,
-                                              int (&nt)[kMapChunks]) {
+                                              int (&nt)[kMapChunks], int (&base)[kMapChunks]) {
 #pragma unroll
   for (int c = 0; c < kMapChunks; ++c) {
     const int bb = lane + 64 * c;
     nt[c] = 0;
-    if (bb < p.n_seqs) nt[c] = min((p.cu[bb + 1] - p.cu[bb] + BR - 1) / BR, p.n_qtiles);
+    base[c] = 0;
+    if (bb < p.n_seqs) {
+      const int len = p.cu[bb + 1] - p.cu[bb];
+      nt[c] = min((len + BR - 1) / BR, p.n_qtiles);
+      if constexpr (PAGED) {
+        const int off = max(min(p.ctx[bb], p.max_ctx) - len, 0);
+        base[c] = (off + p.map_unit - 1) / p.map_unit;
+      }
+    }
   }
 }
 
-__device__ __forceinline__ bool varlen_item(const FwdParams& p, const int (&nt)[kMapChunks], int k,
-                                            int lane, int& qt, int& b) {
-  // A(t) for t = lane + 64 j, by broadcasting each nt_b.
-  int cnt = 0;       // tiles t with A(t) > k
-  int a_next = 0;    // A(qt + 1), found below
-  const int nj = (p.n_qtiles + 63) >> 6;
+__device__ __forceinline__ bool varlen_item(const FwdParams& p, const int (&nt)[kMapChunks],
+                                            const int (&base)[kMapChunks], int k, int lane,
+                                            int& qt, int& b) {
+  const int s = max(p.map_s, 1);  // BR / map_unit, at least 1
+  // A(t) for t = lane + 64 j, by broadcasting each sequence's counts.
+  int cnt = 0;       // keys t with A(t) > k
+  int a_next = 0;    // A(cnt), found below
+  const int nj = (p.map_keys + 63) >> 6;
   for (int j = 0; j < nj; ++j) {
     const int t = lane + 64 * j;
     int a = 0;
@@ -118,28 +140,34 @@ __device__ __forceinline__ bool varlen_item(const FwdParams& p, const int (&nt)[
     for (int c = 0; c < kMapChunks; ++c) {
       if (64 * c >= p.n_seqs) break;  // uniform
       const int nb = min(p.n_seqs - 64 * c, 64);
-      for (int i = 0; i < nb; ++i) a += max(__builtin_amdgcn_readlane(nt[c], i) - t, 0);
+      for (int i = 0; i < nb; ++i) {
+        const int n = __builtin_amdgcn_readlane(nt[c], i);
+        const int d = max(t - __builtin_amdgcn_readlane(base[c], i), 0);
+        a += max(n - (d + s - 1) / s, 0);
+      }
     }
-    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < p.n_qtiles && a > k));
-    // A is non-increasing in t, so the tiles with A(t) > k are 0 .. cnt - 1;
+    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < p.map_keys && a > k));
+    // A is non-increasing in t, so the keys with A(t) > k are 0 .. cnt - 1;
     // A(cnt) is this lane's value where t == cnt.
-    if (__builtin_amdgcn_ballot_w64(t == cnt)) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(t == cnt);
-      a_next = __builtin_amdgcn_readlane(a, __builtin_ctzll(m));
-    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(t == cnt);
+    if (m) a_next = __builtin_amdgcn_readlane(a, __builtin_ctzll(m));
   }
   if (cnt == 0) return false;  // k >= A(0), the number of items
-  qt = cnt - 1;
-  int r = k - (qt + 1 < p.n_qtiles ? a_next : 0);
+  const int key = cnt - 1;
+  int r = k - (cnt < p.map_keys ? a_next : 0);
 #pragma unroll
   for (int c = 0; c < kMapChunks; ++c) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(nt[c] > qt);
+    const int d = key - base[c];
+    const bool has = 64 * c + lane < p.n_seqs && d >= 0 && d % s == 0 && d / s < nt[c];
+    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
     const int n = __builtin_popcountll(m);
     if (r < n) {
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      const uint64_t sel = __builtin_amdgcn_ballot_w64(nt[c] > qt && below == r);
-      b = 64 * c + __builtin_ctzll(sel);
+      const uint64_t sel = __builtin_amdgcn_ballot_w64(has && below == r);
+      const int src = __builtin_ctzll(sel);
+      b = 64 * c + src;
+      qt = __builtin_amdgcn_readlane(d, src) / s;
       return true;
     }
     r -= n;
@@ -198,8 +226,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
   const int xcd = wgi % kXcds;
   const int wx = wgi / kXcds;
   const int nwx = (NW - xcd + kXcds - 1) / kXcds;  // groups on this XCD
-  int nt[kMapChunks];
-  if (p.mapped) varlen_counts(p, lane, BR, nt);
+  int nt[kMapChunks], nbase[kMapChunks];
+  if (p.mapped) varlen_counts<PAGED>(p, lane, BR, nt, nbase);
 
   // Copy offsets (fixed per lane for every item) and LDS bases.
   auto copy_off = [&](int i, int last, bool tr) {
@@ -236,7 +264,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void fwd_kernel(FwdParams p
     const int g = (item % hc) / p.n_chunks;
     int qt, b;
     if (p.mapped) {
-      if (!varlen_item(p, nt, item / hc, lane, qt, b)) continue;  // past the list's end
+      if (!varlen_item(p, nt, nbase, item / hc, lane, qt, b)) continue;  // past the list's end
       qt = __builtin_amdgcn_readfirstlane(qt);
       b = __builtin_amdgcn_readfirstlane(b);
     } else {
@@ -554,8 +582,12 @@ hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t stream) {
   // tile), against n_qtiles * n_seqs slots.
   const long long slots = (long long)p.n_qtiles * a.n_seqs;
   const long long items = std::min<long long>(slots, (long long)a.total_tokens / BR + a.n_seqs);
+  p.map_unit = std::min(BR, kBC);
+  p.map_s = BR / p.map_unit;
+  p.map_keys = (PAGED ? (a.max_ctx_len + p.map_unit - 1) / p.map_unit : 0) +
+               p.map_s * (p.n_qtiles - 1) + 1;
   p.mapped = items < slots && a.n_seqs <= kMapSeqs &&
-             (long long)a.n_seqs * ((p.n_qtiles + 63) / 64) <= 512;
+             (long long)a.n_seqs * ((p.map_keys + 63) / 64) <= 512;
   // Persistent grid: at most one work-group per CU (eight waves) or two
   // (four waves), each walking its share of the items. Items are dealt by
   // their residue mod 8, so the grid is the item count or at least 8.
