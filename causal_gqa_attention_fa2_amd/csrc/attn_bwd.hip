@@ -64,6 +64,7 @@ constexpr int kBK = 128;        // keys per dkdv work-group (4 x 32)
 // wave of the SIMD keeps the matrix core busy between the chain's products.
 constexpr int kDkdvChains = 1;
 constexpr int kBwdThreads = 512;
+constexpr int kKMapChunks = 4;  // ragged-batch lists: up to 256 sequences
 
 struct BwdParams {
   const f16* __restrict__ q;
@@ -90,6 +91,9 @@ struct BwdParams {
   // tiles sorted by work (dkdv_item) instead of every (key tile, sequence)
   // slot; max_qb bounds a key tile's query blocks.
   int kmapped, max_qb;
+  // Ragged batches: 1 when the dq kernels walk the list of non-empty query
+  // tiles (dq_item, at most q_items entries) instead of every slot.
+  int qmapped, q_items;
   float scale, scale_log2;
 };
 
@@ -163,6 +167,60 @@ __device__ __forceinline__ void ds_pack(const float* pv, const f32x16& dpd, f16x
     }
     f[u] = __builtin_bit_cast(f16x8, w);
   }
+}
+
+// The list of a ragged batch's query tiles of BR rows, heaviest first: the
+// pairs (sequence b, query tile qt) with qt * BR < L_b, ordered by qt
+// descending (the tiles with the most keys first), then by b; nt_b =
+// ceil(L_b / BR) (at most n_qtiles) of the sequences lane + 64c are loaded
+// once per work-group. A(t) = sum_b max(nt_b - t, 0) counts the items with
+// tile index >= t, so item k has the largest qt with A(qt) > k, and is the
+// (k - A(qt + 1))-th sequence, by b, with nt_b > qt. Returns false past the
+// end of the list.
+__device__ __forceinline__ void dq_counts(const BwdParams& p, int lane, int BR,
+                                          int (&nt)[kKMapChunks]) {
+#pragma unroll
+  for (int c = 0; c < kKMapChunks; ++c) {
+    const int bb = lane + 64 * c;
+    nt[c] = bb < p.n_seqs ? min((p.cu[bb + 1] - p.cu[bb] + BR - 1) / BR, p.n_qtiles) : 0;
+  }
+}
+
+__device__ __forceinline__ bool dq_item(const BwdParams& p, const int (&nt)[kKMapChunks], int k,
+                                        int lane, int& qt, int& b) {
+  int cnt = 0;     // tiles t with A(t) > k
+  int a_next = 0;  // A(cnt), found below
+  const int nj = (p.n_qtiles + 63) >> 6;
+  for (int j = 0; j < nj; ++j) {
+    const int t = lane + 64 * j;
+    int a = 0;
+#pragma unroll
+    for (int c = 0; c < kKMapChunks; ++c) {
+      if (64 * c >= p.n_seqs) break;  // uniform
+      const int nb = min(p.n_seqs - 64 * c, 64);
+      for (int i = 0; i < nb; ++i) a += max(__builtin_amdgcn_readlane(nt[c], i) - t, 0);
+    }
+    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(t < p.n_qtiles && a > k));
+    const uint64_t m = __builtin_amdgcn_ballot_w64(t == cnt);
+    if (m) a_next = __builtin_amdgcn_readlane(a, __builtin_ctzll(m));
+  }
+  if (cnt == 0) return false;
+  qt = cnt - 1;
+  int r = k - (cnt < p.n_qtiles ? a_next : 0);
+#pragma unroll
+  for (int c = 0; c < kKMapChunks; ++c) {
+    const bool has = nt[c] > qt;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+    const int n = __builtin_popcountll(m);
+    if (r < n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      b = 64 * c + __builtin_ctzll(__builtin_amdgcn_ballot_w64(has && below == r));
+      return true;
+    }
+    r -= n;
+  }
+  return false;
 }
 
 template <int D, bool ROPE = false>
@@ -450,7 +508,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
 //   (0 when c_b < v) counts the items of work >= v, so item k has the largest
 //   work v* with A(v*) > k, and is the (k - A(v* + 1))-th sequence, by b, with
 //   a tile of work exactly v*: (c_b - v*) % 4 == 0 and (c_b - v*) / 4 < nk_b.
-constexpr int kKMapChunks = 4;  // up to 256 sequences
 __device__ __forceinline__ bool dkdv_item(const BwdParams& p, int k, int lane, int& b, int& kt) {
   int cq[kKMapChunks], nk[kKMapChunks];
 #pragma unroll
@@ -937,7 +994,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
   constexpr int kXcds = 8;
   const int BR = 32 * p.nqb;
   const int per = p.n_seqs * p.h_kv * p.n_chunks;
-  const int n_items = p.n_qtiles * per;
+  const int hcq = p.h_kv * p.n_chunks;
+  // Ragged batches: item i is entry i / hcq of the list of non-empty query
+  // tiles, KV head and head chunk from i % hcq.
+  const int n_items = p.qmapped ? p.q_items * hcq : p.n_qtiles * per;
+  int ntq[kKMapChunks];
+  if (p.qmapped) dq_counts(p, (int)threadIdx.x & 63, 32 * p.nqb, ntq);
   const int NW = (int)gridDim.x;
   const int w = (int)blockIdx.x;
   const int xcd = w % kXcds;
@@ -952,12 +1014,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_ds_kernel(BwdParams p) {
   };
   auto decode = [&](int i) {
     Item it;
-    const int qt = p.n_qtiles - 1 - i / per;
-    int rem = i % per;
-    it.chunk = rem % p.n_chunks;
-    rem /= p.n_chunks;
-    it.g = rem % p.h_kv;
-    it.b = rem / p.h_kv;
+    int qt;
+    if (p.qmapped) {
+      const int rem = i % hcq;
+      it.chunk = rem % p.n_chunks;
+      it.g = rem / p.n_chunks;
+      int qq = 0, bb = 0;
+      if (!dq_item(p, ntq, i / hcq, (int)threadIdx.x & 63, qq, bb)) {  // past the list's end
+        it.b = 0;
+        it.s0 = it.L = it.q_wg0 = it.n_kt = 0;
+        return it;
+      }
+      qt = __builtin_amdgcn_readfirstlane(qq);
+      it.b = __builtin_amdgcn_readfirstlane(bb);
+    } else {
+      qt = p.n_qtiles - 1 - i / per;
+      int rem = i % per;
+      it.chunk = rem % p.n_chunks;
+      rem /= p.n_chunks;
+      it.g = rem % p.h_kv;
+      it.b = rem / p.h_kv;
+    }
     it.s0 = load_uniform(p.cu, it.b);
     it.L = load_uniform(p.cu, it.b + 1) - it.s0;
     it.q_wg0 = qt * BR;
@@ -1139,7 +1216,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.n_ktiles = (a.max_seqlen + kBK - 1) / kBK;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  const int n_items = p.n_qtiles * a.n_seqs * a.h_kv * p.n_chunks;
+  // Ragged batches: the list of non-empty query tiles has at most
+  // floor(T / BR) + n_seqs entries, against n_qtiles * n_seqs slots.
+  const int BRq = 32 * p.nqb;
+  const long long qslots = (long long)p.n_qtiles * a.n_seqs;
+  const long long qitems = std::min<long long>(qslots, (long long)a.total_tokens / BRq + a.n_seqs);
+  // (only the dq-from-dS kernel of the ragged path walks the list)
+  p.qmapped = a.ds != nullptr && qitems < qslots && a.n_seqs <= 64 * kKMapChunks &&
+              (long long)a.n_seqs * ((p.n_qtiles + 63) / 64) <= 512;
+  p.q_items = (int)qitems;
+  const int n_items = (int)((p.qmapped ? qitems : qslots) * a.h_kv * p.n_chunks);
   // Persistent dq grids; items are dealt by their residue mod 8, so the grid
   // is the item count or at least 8.
   const int resident = a.num_cus > 8 ? a.num_cus : 8;

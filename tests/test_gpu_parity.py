@@ -88,6 +88,26 @@ def test_long_batch_group_sizes(gpu, h_q, h_kv, d):
     check_bwd(name, inp, dq, dk, dv)
 
 
+@pytest.mark.parametrize("n_seqs,h_q,h_kv,d", [(150, 4, 2, 64), (256, 8, 2, 128),
+                                                (257, 2, 1, 64)], ids=lambda x: str(x))
+def test_many_unequal_sequences(gpu, n_seqs, h_q, h_kv, d):
+    """Many short sequences and four long ones: the work-sorted lists of
+    query and key tiles span several groups of 64 sequences (256 is the most
+    they take; 257 falls back to the static order). Compared in full."""
+    g = np.random.default_rng(2400 + n_seqs)
+    lens = [int(x) for x in g.integers(0, 41, size=n_seqs)]
+    for i in g.choice(n_seqs, size=4, replace=False):
+        lens[int(i)] = int(g.integers(300, 700))
+    name = f"{n_seqs} seqs hq{h_q} hkv{h_kv} d{d}"
+    inp = W.make_train_inputs(lens, h_q, h_kv, d, seed=2400 + n_seqs)
+    dd = dev(inp, gpu)
+    o, lse = gpu_fwd(dd)
+    dq, dk, dv = gpu_bwd(dd, o, lse)
+    torch.cuda.synchronize()
+    check_fwd(name, inp, o, lse)
+    check_bwd(name, inp, dq, dk, dv)
+
+
 def test_tiny_workload(gpu):
     inp = W.workload_inputs("tiny")
     dd = dev(inp, gpu)
