@@ -88,18 +88,26 @@ def test_long_batch_group_sizes(gpu, h_q, h_kv, d):
     check_bwd(name, inp, dq, dk, dv)
 
 
-@pytest.mark.parametrize("n_seqs,h_q,h_kv,d", [(150, 4, 2, 64), (256, 8, 2, 128),
-                                                (257, 2, 1, 64)], ids=lambda x: str(x))
-def test_many_unequal_sequences(gpu, n_seqs, h_q, h_kv, d):
+@pytest.mark.parametrize("n_seqs,h_q,h_kv,d,longest", [
+    (150, 4, 2, 64, 0), (256, 8, 2, 128, 0), (257, 2, 1, 64, 0), (256, 2, 1, 64, 4200)],
+    ids=lambda x: str(x))
+def test_many_unequal_sequences(gpu, n_seqs, h_q, h_kv, d, longest):
     """Many short sequences and four long ones: the work-sorted lists of
     query and key tiles span several groups of 64 sequences (256 is the most
-    they take; 257 falls back to the static order). Compared in full."""
-    g = np.random.default_rng(2400 + n_seqs)
+    they take; 257 falls back to the static order). With one sequence of
+    4200 tokens the forward walks its list in the eight-wave shape, the dS
+    blocks would pass their 4 GiB bound (so the backward recomputes), and
+    the key-tile list passes its size bound (256 sequences x 3 groups of 64
+    query blocks), so dK/dV falls back to the static order. Compared in
+    full."""
+    g = np.random.default_rng(2400 + n_seqs + longest)
     lens = [int(x) for x in g.integers(0, 41, size=n_seqs)]
     for i in g.choice(n_seqs, size=4, replace=False):
         lens[int(i)] = int(g.integers(300, 700))
-    name = f"{n_seqs} seqs hq{h_q} hkv{h_kv} d{d}"
-    inp = W.make_train_inputs(lens, h_q, h_kv, d, seed=2400 + n_seqs)
+    if longest:
+        lens[int(g.integers(0, n_seqs))] = longest
+    name = f"{n_seqs} seqs hq{h_q} hkv{h_kv} d{d} longest {max(lens)}"
+    inp = W.make_train_inputs(lens, h_q, h_kv, d, seed=2400 + n_seqs + longest)
     dd = dev(inp, gpu)
     o, lse = gpu_fwd(dd)
     dq, dk, dv = gpu_bwd(dd, o, lse)
