@@ -89,6 +89,16 @@ def test_bwd_workspace(lib):
     # Equal lengths keep the recompute path and its small workspace.
     eq = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(8, 8192, 1024, 16, 8, 128)))
     assert eq == 2 * ((16 * 8192 * 4 + 255) // 256 * 256)
+    # The dS blocks are bounded by 4 GiB: 2 sequences x 16 heads x 256^2 blocks
+    # of 2 KiB is exactly that and keeps the dS path; one more 32-row block
+    # (257^2) or a batch far above it (256 x 2 x 132^2) recomputes instead.
+    row_t = lambda h, t: (h * t * 4 + 255) // 256 * 256
+    at = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(2, 8292, 8192, 16, 8, 128)))
+    assert at == 2 * row_t(16, 8292) + (4 << 30)
+    past = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(2, 8293, 8193, 16, 8, 128)))
+    assert past == 2 * row_t(16, 8293)
+    big = lib.attn_bwd_workspace_bytes(ctypes.byref(VarlenDims(256, 11089, 4200, 2, 1, 64)))
+    assert big == 2 * row_t(2, 11089)
     p = ctypes.c_void_p
     args = [p(FAKE)] * 7 + [p(FAKE)] * 3
 
